@@ -1,0 +1,359 @@
+/*
+ * qsa_ref.c — CPU oracle of the QSA indexer hot path.  TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the reference the GPU library is checked against.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it; the product path never
+ * does.  It shares no code, header or constant with the GPU library.
+ *
+ * It is the plain definition of what the "Qsa Indexer Kernels" page (TensorRT-Edge-LLM C++ API
+ * documentation) says the kernels compute, written as slow straight-line C:
+ *   - ref_q_prep        launchQsaIndexQPrep (K1a),
+ *   - ref_k_compress    launchQsaIndexKCompress (K1b), and with a pool
+ *                       launchQsaIndexKCompressPaged,
+ *   - ref_persist       launchQsaRawKTailWritePrefill (raw-K tails) and the kbar V-tail write,
+ *   with the pool addressing of struct QsaIndexerPoolState.
+ *
+ * Numerics (the page: "FP32 unless stated"; readings where it is open are listed beside each
+ * step):
+ *   - Build with -ffp-contract=off -fno-fast-math on x86-64 (SSE): every float operation below
+ *     is one IEEE binary32 operation rounded to nearest even; no FMA, no reassociation.
+ *   - The sum of squares (reduction order left open by the page) is accumulated in binary64,
+ *     where each product of two widened T values is exact, and rounded once to binary32.
+ *   - rsqrtf (an approximate intrinsic on the page's hardware) is taken as the correctly
+ *     rounded binary32 value of 1/sqrt(v), evaluated in binary64 and rounded once.
+ *   - Conversions between binary32 and T are written below from the IEEE 754 definitions:
+ *     widening is exact; narrowing rounds to nearest, ties to even, keeps subnormals, and maps
+ *     NaN to a quiet NaN.
+ * OpenMP splits rows and blocks over threads; every output element is written by exactly one
+ * iteration, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define REF_F16 0
+#define REF_BF16 1
+
+enum { HEADS = 4, DIM = 128, ROW = 640, KCOL = 512, HALF_ROPE = 32, CS_W = 64, RATIO = 4,
+       PAGE = 128 };
+
+/* Mirror of the page's QsaIndexerPoolState (declared here on its own, not shared). */
+typedef struct {
+  void* poolPtr;
+  const int32_t* pageTable;
+  int32_t maxPagesPerSeq;
+  int32_t numPages;
+  int32_t numKVHeads;
+  int32_t poolHeadDim;
+  int32_t headSize;
+} ref_pool_t;
+
+/* ---------------------------------------------------------------- IEEE conversions ---- */
+
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bfloat16 is the top half of a binary32: widening appends 16 zero bits. */
+static float bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static float f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h >> 15) << 31;
+  uint32_t e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  if (e == 0x1f) /* inf or NaN: keep the payload, quiet the NaN */
+    return bits_f32(sign | 0x7f800000u | (m << 13) | (m ? 0x00400000u : 0u));
+  /* zero, subnormal (m * 2^-24) or normal ((1024 + m) * 2^(e-25)); all exact in binary32 */
+  double mag = (e == 0) ? ldexp((double)m, -24) : ldexp((double)(0x400 | m), (int)e - 25);
+  float f = (float)mag;
+  return bits_f32(sign | f32_bits(f));
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even. */
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u = f32_bits(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN */
+  uint32_t keep = u >> 16, rest = u & 0xffffu;
+  if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u; /* carries into exp */
+  return (uint16_t)keep;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, with subnormals and overflow to inf. */
+static uint16_t f32_to_f16(float f) {
+  uint32_t u = f32_bits(f);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u | ((a >> 13) & 0x3ffu)); /* NaN */
+  if (a == 0x7f800000u) return (uint16_t)(sign | 0x7c00u);                       /* inf */
+  if (a < 0x00800000u) return sign; /* |f| < 2^-126: far below half the smallest subnormal */
+  int e = (int)(a >> 23) - 127;               /* |f| = sig * 2^(e-23), sig in [2^23, 2^24) */
+  uint32_t sig = (a & 0x7fffffu) | 0x800000u;
+  /* binary16 keeps 11 significant bits for a normal result (e >= -14); below that the
+   * quantum is fixed at 2^-24, so the number of dropped bits grows by one per binade. */
+  int drop = (e >= -14) ? 13 : 13 + (-14 - e);
+  if (drop > 24) return sign; /* |f| < 2^-25 = half the smallest subnormal: rounds to 0 */
+  uint32_t q = sig >> drop, rem = sig & ((1u << drop) - 1u), half = 1u << (drop - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1u;
+  if (e >= -14) {
+    uint32_t E = (uint32_t)(e + 15);
+    if (q == 0x800u) { q = 0x400u; E += 1u; } /* rounding carried into the next binade */
+    if (E >= 31u) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (E << 10) | (q & 0x3ffu));
+  }
+  return (uint16_t)(sign | q); /* subnormal; q == 0x400 is exactly the smallest normal */
+}
+
+static float widen(uint16_t h, int dt) { return dt == REF_BF16 ? bf16_to_f32(h) : f16_to_f32(h); }
+static uint16_t narrow(float f, int dt) { return dt == REF_BF16 ? f32_to_bf16(f) : f32_to_f16(f); }
+
+/* ------------------------------------------------------ norm + rope of one 128-vector ---- */
+
+/*
+ * Gemma-style RMSNorm with (1 + w) gamma, then partial neox rope, then one cast to T
+ * ("Qsa Indexer Kernels": launchQsaIndexQPrep, "Exact numerics"; reused verbatim by
+ * launchQsaIndexKCompress on the cast block mean).
+ *   meanSq = sum_d x_d^2 / 128; inv = rsqrt(meanSq + eps); y_d = (x_d * inv) * (1 + w_d)
+ *   o_i = y_i*cos_i - y_{i+32}*sin_i, o_{i+32} = y_{i+32}*cos_i + y_i*sin_i (i < 32)
+ *   o_d = y_d (d >= 64); out_d = T(o_d).
+ * cs is the 64-float cosSin row of the rope position: cos in [0,32), sin in [32,64).
+ * dbg (nullable): meanSq, inv, and the 128 pre-cast values.
+ */
+static void norm_rope(const float* x, const uint16_t* w, const float* cs, float eps, int dt,
+                      uint16_t* out, float* dbgMeanSq, float* dbgInv, float* dbgPre) {
+  double acc = 0.0;
+  for (int d = 0; d < DIM; ++d) acc += (double)x[d] * (double)x[d];
+  float sumSq = (float)acc;
+  float meanSq = sumSq / 128.0f;
+  float v = meanSq + eps;
+  float inv = (float)(1.0 / sqrt((double)v));
+  float y[DIM], o[DIM];
+  for (int d = 0; d < DIM; ++d) {
+    float w1 = 1.0f + widen(w[d], dt);
+    float xs = x[d] * inv;
+    y[d] = xs * w1;
+  }
+  for (int i = 0; i < HALF_ROPE; ++i) {
+    float c = cs[i], s = cs[HALF_ROPE + i];
+    float a0 = y[i] * c, b0 = y[i + HALF_ROPE] * s;
+    float a1 = y[i + HALF_ROPE] * c, b1 = y[i] * s;
+    o[i] = a0 - b0;
+    o[i + HALF_ROPE] = a1 + b1;
+  }
+  for (int d = 2 * HALF_ROPE; d < DIM; ++d) o[d] = y[d];
+  for (int d = 0; d < DIM; ++d) out[d] = narrow(o[d], dt);
+  if (dbgMeanSq) *dbgMeanSq = meanSq;
+  if (dbgInv) *dbgInv = inv;
+  if (dbgPre) memcpy(dbgPre, o, sizeof o);
+}
+
+/* ----------------------------------------------------------------------------- K1a ---- */
+
+/*
+ * launchQsaIndexQPrep: for each (b, t), rows t >= clamp(ctx[b], 0, S) are written as +0 and
+ * their input is not read; otherwise each of the 4 heads (columns [128h, 128h+128)) goes
+ * through norm_rope with wQ and the cosSin row of position t.
+ * Debug outputs (each nullable): meanSq/inv [B,S,4], preCast [B,S,4,128]; zeros on padding.
+ */
+void ref_q_prep(uint16_t* qNormed, const uint16_t* indexQk, const float* cosSin,
+                int32_t maxPositions, const int32_t* ctx, const uint16_t* wQ, float eps,
+                int32_t B, int32_t S, int dt, float* dbgMeanSq, float* dbgInv, float* dbgPre) {
+  (void)maxPositions;
+  int64_t rows = (int64_t)B * S;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    int64_t b = r / S, t = r % S;
+    int64_t L = ctx[b] < 0 ? 0 : (ctx[b] > S ? S : ctx[b]);
+    uint16_t* out = qNormed + r * (HEADS * DIM);
+    if (t >= L) {
+      memset(out, 0, sizeof(uint16_t) * HEADS * DIM);
+      if (dbgMeanSq) memset(dbgMeanSq + r * HEADS, 0, sizeof(float) * HEADS);
+      if (dbgInv) memset(dbgInv + r * HEADS, 0, sizeof(float) * HEADS);
+      if (dbgPre) memset(dbgPre + r * HEADS * DIM, 0, sizeof(float) * HEADS * DIM);
+      continue;
+    }
+    for (int h = 0; h < HEADS; ++h) {
+      float x[DIM];
+      for (int d = 0; d < DIM; ++d) x[d] = widen(indexQk[r * ROW + h * DIM + d], dt);
+      norm_rope(x, wQ, cosSin + t * CS_W, eps, dt, out + h * DIM,
+                dbgMeanSq ? dbgMeanSq + r * HEADS + h : 0, dbgInv ? dbgInv + r * HEADS + h : 0,
+                dbgPre ? dbgPre + (r * HEADS + h) * DIM : 0);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------- pool addressing ---- */
+
+/*
+ * QsaIndexerPoolState addressing: element (page, row, head, col) of the
+ * [2*numPages, 128, numKVHeads, poolHeadDim] pool is at
+ * page*128*H*D + row*H*D + head*D + col; the indexer state is head 0, columns
+ * [headSize, headSize+128).  Returns the element offset of column headSize of the tail row of
+ * position pos in plane `plane`, or -1 when the page-table slot is out of range or the entry is
+ * unused (-1) or outside [0, 2*numPages): nothing is persisted then.
+ */
+static int64_t pool_tail_offset(const ref_pool_t* p, int64_t b, int plane, int64_t pos) {
+  int64_t slot = pos / PAGE; /* pos >= 0 here, so this is pos >> 7 */
+  if (slot < 0 || slot >= p->maxPagesPerSeq) return -1;
+  int32_t id = p->pageTable[(b * 2 + plane) * p->maxPagesPerSeq + slot];
+  if (id == -1 || id < 0 || (int64_t)id >= 2 * (int64_t)p->numPages) return -1;
+  int64_t HD = (int64_t)p->numKVHeads * p->poolHeadDim;
+  int64_t row = pos % PAGE;
+  return ((int64_t)id * PAGE + row) * HD + 0 * p->poolHeadDim + p->headSize;
+}
+
+/* ----------------------------------------------------------------------------- K1b ---- */
+
+/* The block triplet of sequence b: the scalars, or entry b of the per-sequence arrays. */
+static void triplet(int64_t b, int32_t bB, int32_t bE, int32_t pl, const int32_t* pastLens,
+                    const int32_t* blockBegins, const int32_t* blockEnds, int32_t maxSpan,
+                    int64_t* gB, int64_t* gE, int64_t* p) {
+  if (pastLens) {
+    *gB = blockBegins[b];
+    *gE = blockEnds[b];
+    if (*gE > *gB + maxSpan) *gE = *gB + maxSpan;
+    *p = pastLens[b];
+  } else {
+    *gB = bB; *gE = bE; *p = pl;
+  }
+}
+
+/*
+ * launchQsaIndexKCompress validity: the block is complete and fully inside the provided rows,
+ * 4g+3 < ctx and 4g >= pastLen; "inside the provided rows" also bounds the last row,
+ * 4g+3-pastLen < S; and the rope row 4g must exist in cosSin (checkMaxPos).
+ */
+static int block_valid(int64_t g, int64_t ctx, int64_t p, int64_t S, int64_t maxPos,
+                       int checkMaxPos) {
+  int64_t t0 = 4 * g;
+  if (!(t0 + 3 < ctx)) return 0;
+  if (!(t0 >= p)) return 0;
+  if (!(t0 + 3 - p < S)) return 0;
+  if (checkMaxPos && !(t0 < maxPos)) return 0;
+  return 1;
+}
+
+/*
+ * launchQsaIndexKCompress / launchQsaIndexKCompressPaged: for each b and each g in the block
+ * range (skipping g outside [0, numBlocks)), an invalid block writes 128 zeros and reads
+ * nothing; a valid block forms, per dim d, s = ((k0+k1)+k2)+k3 in binary32 in that order,
+ * mean = s * 0.25, m_T = T(mean), m = f32(m_T), then norm_rope(m) with wK at position 4g.
+ * With a pool, each valid block's kbar row is also copied bit for bit to its V-tail (plane 1,
+ * position 4g) when the page guard passes.
+ * Debug outputs (nullable): mT [B,nb,128] (T), meanSq/inv [B,nb], preCast [B,nb,128].
+ */
+void ref_k_compress(uint16_t* kbar, const uint16_t* indexQk, const float* cosSin,
+                    int32_t maxPositions, const int32_t* ctx, const uint16_t* wK, float eps,
+                    int32_t B, int32_t S, int32_t numBlocks, int32_t blockBegin, int32_t blockEnd,
+                    int32_t pastLen, const int32_t* pastLens, const int32_t* blockBegins,
+                    const int32_t* blockEnds, int32_t maxBlockSpan, const ref_pool_t* pool,
+                    int dt, uint16_t* dbgMT, float* dbgMeanSq, float* dbgInv, float* dbgPre) {
+  int64_t span = pastLens ? maxBlockSpan : (int64_t)blockEnd - blockBegin;
+  if (span <= 0) return;
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < (int64_t)B * span; ++u) {
+    int64_t b = u / span, gB, gE, p;
+    triplet(b, blockBegin, blockEnd, pastLen, pastLens, blockBegins, blockEnds, maxBlockSpan,
+            &gB, &gE, &p);
+    int64_t g = gB + u % span;
+    if (g >= gE || g < 0 || g >= numBlocks) continue;
+    int64_t o = b * numBlocks + g;
+    uint16_t* out = kbar + o * DIM;
+    if (!block_valid(g, ctx[b], p, S, maxPositions, 1)) {
+      memset(out, 0, sizeof(uint16_t) * DIM);
+      if (dbgMT) memset(dbgMT + o * DIM, 0, sizeof(uint16_t) * DIM);
+      if (dbgMeanSq) dbgMeanSq[o] = 0.0f;
+      if (dbgInv) dbgInv[o] = 0.0f;
+      if (dbgPre) memset(dbgPre + o * DIM, 0, sizeof(float) * DIM);
+      continue;
+    }
+    const uint16_t* k[RATIO];
+    for (int j = 0; j < RATIO; ++j) k[j] = indexQk + ((b * S) + (4 * g + j - p)) * ROW + KCOL;
+    float m[DIM];
+    for (int d = 0; d < DIM; ++d) {
+      float k0 = widen(k[0][d], dt), k1 = widen(k[1][d], dt);
+      float k2 = widen(k[2][d], dt), k3 = widen(k[3][d], dt);
+      float s = k0 + k1;
+      s = s + k2;
+      s = s + k3;
+      float mean = s * 0.25f;
+      uint16_t mT = narrow(mean, dt);
+      if (dbgMT) dbgMT[o * DIM + d] = mT;
+      m[d] = widen(mT, dt);
+    }
+    norm_rope(m, wK, cosSin + 4 * g * CS_W, eps, dt, out, dbgMeanSq ? dbgMeanSq + o : 0,
+              dbgInv ? dbgInv + o : 0, dbgPre ? dbgPre + o * DIM : 0);
+    if (pool) {
+      int64_t off = pool_tail_offset(pool, b, 1, 4 * g);
+      if (off >= 0) memcpy((uint16_t*)pool->poolPtr + off, out, sizeof(uint16_t) * DIM);
+    }
+  }
+}
+
+/* --------------------------------------------------------------------------- persist ---- */
+
+/*
+ * launchQsaRawKTailWritePrefill, generalised to a past length: tokens
+ * t in [max(p, ctx - ctx%4), ctx) with 0 <= t-p < S copy indexQk row t-p, columns
+ * [512, 640), bit-unmodified to their K-tail (plane 0, position t).
+ * With kbar: every valid block of the range (validity without the cosSin clause) copies its
+ * dense kbar row bit for bit to its V-tail (plane 1, position 4g).  Guards as
+ * pool_tail_offset; no other cell changes.
+ */
+void ref_persist(const ref_pool_t* pool, const uint16_t* indexQk, const uint16_t* kbar,
+                 const int32_t* ctx, int32_t B, int32_t S, int32_t numBlocks, int32_t blockBegin,
+                 int32_t blockEnd, int32_t pastLen, const int32_t* pastLens,
+                 const int32_t* blockBegins, const int32_t* blockEnds, int32_t maxBlockSpan) {
+  uint16_t* base = (uint16_t*)pool->poolPtr;
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t gB, gE, p;
+    triplet(b, blockBegin, blockEnd, pastLen, pastLens, blockBegins, blockEnds, maxBlockSpan,
+            &gB, &gE, &p);
+    int64_t c = ctx[b];
+    if (c > 0) {
+      int64_t t0 = c - c % 4;
+      if (t0 < p) t0 = p;
+      for (int64_t t = t0; t < c; ++t) {
+        int64_t r = t - p;
+        if (r < 0 || r >= S) continue;
+        int64_t off = pool_tail_offset(pool, b, 0, t);
+        if (off >= 0)
+          memcpy(base + off, indexQk + (b * S + r) * ROW + KCOL, sizeof(uint16_t) * DIM);
+      }
+    }
+    if (!kbar) continue;
+    for (int64_t g = gB; g < gE; ++g) {
+      if (g < 0 || g >= numBlocks) continue;
+      if (!block_valid(g, c, p, S, 0, 0)) continue;
+      int64_t off = pool_tail_offset(pool, b, 1, 4 * g);
+      if (off >= 0) memcpy(base + off, kbar + (b * numBlocks + g) * DIM, sizeof(uint16_t) * DIM);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------- utilities ---- */
+
+/* Element-wise conversions, exported so the tests can pin them against library routines. */
+void ref_widen(const uint16_t* in, float* out, int64_t n, int dt) {
+  for (int64_t i = 0; i < n; ++i) out[i] = widen(in[i], dt);
+}
+void ref_narrow(const float* in, uint16_t* out, int64_t n, int dt) {
+  for (int64_t i = 0; i < n; ++i) out[i] = narrow(in[i], dt);
+}
+
+void ref_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int ref_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,406 @@
+"""Pins of the CPU oracle: checks that tie it to facts other than itself.
+
+Each ``check_*`` takes an oracle object (``oracle.ref.Oracle``) and raises AssertionError when
+the oracle breaks the fact it pins.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` runs them on deliberately broken builds of it and requires that each
+break is caught.  The facts come from the "Qsa Indexer Kernels" page (TensorRT-Edge-LLM C++ API
+documentation) and from mathematics:
+  - hand-worked values (tests/golden/hand_worked.json),
+  - closed forms (quarter-turn rope, w = -1, all-ones heads),
+  - invariants (power-of-two scale invariance, padding never read, sub-range union, ranges
+    mode = separate calls, thread-count independence, K1a/K1b agreement on constant blocks),
+  - an independent numpy re-derivation on the tiny prefill workload,
+  - the pool round trip through an independent tensor view of the addressing contract.
+"""
+import json
+import os
+
+import numpy as np
+
+from tests import numpy_model as nm
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
+H = lambda s: int(s, 16)  # noqa: E731
+
+
+def _zero_row(B=1, S=4):
+    return np.zeros((B, S, 640), np.uint16)
+
+
+def _id_table(n):
+    """cosSin rows with cos = 1, sin = 0 (rope is the identity)."""
+    cs = np.zeros((n, 64), np.float32)
+    cs[:, :32] = 1.0
+    return cs
+
+
+def _rand_bits(rng, shape, dt, scale=1.0):
+    from sparse_attention_indexer_qsa_amd.workloads import to_bits
+    return to_bits(scale * rng.standard_normal(shape, dtype=np.float32), dt)
+
+
+def _is_zero(bits):
+    return np.all((bits & 0x7FFF) == 0)
+
+
+# ------------------------------------------------------------------------ hand-worked ----
+
+def check_block_mean_order(O):
+    for c in GOLDEN["block_mean_order"]["cases"]:
+        x = _zero_row()
+        x[0, :, 512] = [H(v) for v in c["k"]]
+        cs = _id_table(4)
+        _, dbg = O.k_compress(x, cs, np.array([4]), np.zeros(128, np.uint16), 1e-6, 1, 0, 1, 0,
+                              c["dt"], debug=True)
+        assert dbg["mT"][0, 0, 0] == H(c["mT"]), (c, hex(dbg["mT"][0, 0, 0]))
+
+
+def check_kbar_order_end_to_end(O):
+    means = {c["dt"]: c for c in GOLDEN["block_mean_order"]["cases"] if c["mT"] != c["k"][0]}
+    for c in GOLDEN["kbar_order_end_to_end"]["cases"]:
+        x = _zero_row()
+        x[0, :, 512] = [H(v) for v in means[c["dt"]]["k"]]
+        x[0, :, 513] = H(c["d1"])
+        kb = O.k_compress(x, _id_table(4), np.array([4]), np.zeros(128, np.uint16), 1e-6, 1,
+                          0, 1, 0, c["dt"])
+        assert [int(v) for v in kb[0, 0, :2]] == [H(v) for v in c["kbar01"]], c
+        assert _is_zero(kb[0, 0, 2:])
+        # the fixture discriminates: an input whose fixed-order mean is the pairwise mean
+        # gives the other answer
+        x2 = x.copy()
+        x2[0, :, 512] = H(means[c["dt"]]["mT_if_pairwise"])   # four equal rows: mean exact
+        kb2 = O.k_compress(x2, _id_table(4), np.array([4]), np.zeros(128, np.uint16), 1e-6, 1,
+                           0, 1, 0, c["dt"])
+        assert [int(v) for v in kb2[0, 0, :2]] == [H(v) for v in c["kbar01_if_pairwise"]], c
+
+
+def check_norm_closed_forms(O):
+    for c in GOLDEN["norm_closed_forms"]["cases"]:
+        one = 0x3F80 if c["dt"] == "bf16" else 0x3C00
+        x = _zero_row(1, 1)
+        if "out_all" in c:
+            x[0, 0, :512] = one
+        else:
+            x[0, 0, [0, 128, 256, 384]] = one
+        q = O.q_prep(x, _id_table(1), np.array([1]), np.zeros(128, np.uint16), 1e-6, c["dt"])
+        if "out_all" in c:
+            assert np.all(q == H(c["out_all"])), c
+        else:
+            assert np.all(q[0, 0, :, 0] == H(c["out0"])), (c, q[0, 0, :, 0])
+            assert _is_zero(q[0, 0, :, 1:])
+
+
+def check_gamma_minus_one_gives_zeros(O):
+    rng = np.random.default_rng(7)
+    for dt in ("bf16", "f16"):
+        minus1 = 0xBF80 if dt == "bf16" else 0xBC00
+        x = _rand_bits(rng, (1, 8, 640), dt)
+        from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+        cs = cos_sin_table(32, 1e4)
+        q = O.q_prep(x, cs, np.array([8]), np.full(128, minus1, np.uint16), 1e-6, dt)
+        assert _is_zero(q)
+        kb = O.k_compress(x, cs, np.array([8]), np.full(128, minus1, np.uint16), 1e-6, 2, 0, 2,
+                          0, dt)
+        assert _is_zero(kb)
+
+
+# ------------------------------------------------------------------------- invariants ----
+
+def check_scale_invariance(O):
+    """With eps = 0, scaling x by 2^k scales meanSq by 4^k and rsqrt by 2^-k exactly, so the
+    output bits do not change (no underflow or overflow in the chosen range)."""
+    rng = np.random.default_rng(11)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    cs = cos_sin_table(16, 1e4)
+    for dt in ("bf16", "f16"):
+        base = rng.standard_normal((1, 16, 640), dtype=np.float32)
+        w = _rand_bits(rng, 128, dt, 0.1)
+        ref_q = O.q_prep(_bits(base, dt), cs, np.array([16]), w, 0.0, dt)
+        ref_k = O.k_compress(_bits(base, dt), cs, np.array([16]), w, 0.0, 4, 0, 4, 0, dt)
+        for k in (-3, 2, 5):
+            xs = _bits(base * np.float32(2.0 ** k), dt)
+            assert np.array_equal(O.q_prep(xs, cs, np.array([16]), w, 0.0, dt), ref_q), (dt, k)
+            assert np.array_equal(O.k_compress(xs, cs, np.array([16]), w, 0.0, 4, 0, 4, 0, dt),
+                                  ref_k), (dt, k)
+
+
+def _bits(values, dt):
+    from sparse_attention_indexer_qsa_amd.workloads import to_bits
+    return to_bits(values, dt)
+
+
+def check_rope_quarter_turn(O):
+    """cos = 0, sin = 1 is an exact quarter turn of each pair (i, i+32): o_i = -y_{i+32},
+    o_{i+32} = y_i; dims 64..127 are untouched; compared with the identity row cos=1, sin=0."""
+    rng = np.random.default_rng(13)
+    for dt in ("bf16", "f16"):
+        x = _rand_bits(rng, (1, 2, 640), dt)
+        w = _rand_bits(rng, 128, dt, 0.1)
+        ident = _id_table(2)
+        turn = np.zeros((2, 64), np.float32)
+        turn[:, 32:] = 1.0
+        _, d0 = O.q_prep(x, ident, np.array([2]), w, 1e-6, dt, debug=True)
+        _, d1 = O.q_prep(x, turn, np.array([2]), w, 1e-6, dt, debug=True)
+        y, o = d0["preCast"], d1["preCast"]
+        assert np.array_equal(o[..., :32], -y[..., 32:64])
+        assert np.array_equal(o[..., 32:64], y[..., :32])
+        assert np.array_equal(o[..., 64:], y[..., 64:])
+
+
+def check_rope_position_and_pair_norm(O):
+    """Token t uses cosSin row t (a one-row call on the table shifted to start at t gives the
+    same bits), and each rope pair keeps its norm to binary32 rounding."""
+    rng = np.random.default_rng(17)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    cs = cos_sin_table(64, 1e4)
+    dt = "bf16"
+    x = _rand_bits(rng, (1, 64, 640), dt)
+    w = _rand_bits(rng, 128, dt, 0.1)
+    q, dq = O.q_prep(x, cs, np.array([64]), w, 1e-6, dt, debug=True)
+    _, did = O.q_prep(x, _id_table(64), np.array([64]), w, 1e-6, dt, debug=True)
+    for t in (1, 17, 63):
+        qt = O.q_prep(x[:, t:t + 1], cs[t:t + 1], np.array([1]), w, 1e-6, dt)
+        assert np.array_equal(qt[0, 0], q[0, t])
+    y, o = did["preCast"].astype(np.float64), dq["preCast"].astype(np.float64)
+    ny = y[..., :32] ** 2 + y[..., 32:64] ** 2
+    no = o[..., :32] ** 2 + o[..., 32:64] ** 2
+    assert np.allclose(no, ny, rtol=2e-6, atol=1e-30)
+    assert not np.array_equal(o[..., :64], y[..., :64])
+
+
+def check_padding_zero_and_never_read(O):
+    """Rows t >= ctx (and blocks that are not complete inside the rows) are +0 and their input
+    is never read: NaN or other garbage there changes no output bit."""
+    rng = np.random.default_rng(19)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    cs = cos_sin_table(32, 1e4)
+    for dt in ("bf16", "f16"):
+        nan = 0x7FC0 if dt == "bf16" else 0x7E00
+        x = _rand_bits(rng, (4, 32, 640), dt)
+        ctx = np.array([0, 13, 32, 30], np.int32)
+        w = _rand_bits(rng, 128, dt, 0.1)
+        xa, xb = x.copy(), x.copy()
+        for b, c in enumerate(ctx):
+            xa[b, c:] = nan
+            xb[b, c:] = rng.integers(0, 65536, (32 - c, 640)).astype(np.uint16)
+        qa = O.q_prep(xa, cs, ctx, w, 1e-6, dt)
+        qb = O.q_prep(xb, cs, ctx, w, 1e-6, dt)
+        assert np.array_equal(qa, qb)
+        for b, c in enumerate(ctx):
+            assert np.all(qa[b, c:] == 0)
+            assert all(not _is_zero(qa[b, t]) for t in range(c))
+        ka = O.k_compress(xa, cs, ctx, w, 1e-6, 8, 0, 8, 0, dt)
+        kb = O.k_compress(xb, cs, ctx, w, 1e-6, 8, 0, 8, 0, dt)
+        assert np.array_equal(ka, kb)
+        for b, c in enumerate(ctx):
+            nvalid = c // 4
+            assert np.all(ka[b, nvalid:] == 0)
+            assert all(not _is_zero(ka[b, g]) for g in range(nvalid))
+        # lengths outside [0, S] are clamped for K1a
+        q_over = O.q_prep(x, cs, np.array([40, -5, 32, 32]), w, 1e-6, dt)
+        q_ref = O.q_prep(x, cs, np.array([32, 0, 32, 32]), w, 1e-6, dt)
+        assert np.array_equal(q_over, q_ref)
+
+
+def check_block_validity_rule(O):
+    """launchQsaIndexKCompress: valid iff 4g+3 < ctx and 4g >= pastLen (and the block's rows
+    lie inside the S provided rows); the raw key of token 4g+j is row 4g+j-pastLen."""
+    rng = np.random.default_rng(23)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    dt = "bf16"
+    cs = cos_sin_table(64, 1e4)
+    w = _rand_bits(rng, 128, dt, 0.1)
+    full = _rand_bits(rng, (1, 64, 640), dt)
+    ref = O.k_compress(full, cs, np.array([64]), w, 1e-6, 16, 0, 16, 0, dt)
+    # (ctx, pastLen, S rows given, expected valid blocks among [0, 16))
+    cases = [(64, 0, 64, set(range(16))), (63, 0, 64, set(range(15))),
+             (64, 8, 56, set(range(2, 16))), (64, 9, 55, set(range(3, 16))),
+             (40, 8, 20, set(range(2, 7))), (64, 12, 8, {3, 4}), (3, 0, 64, set())]
+    for ctx, p, S, valid in cases:
+        rows = full[:, p:p + S]
+        kb = O.k_compress(rows, cs, np.array([ctx]), w, 1e-6, 16, 0, 16, p, dt)
+        for g in range(16):
+            if g in valid:
+                assert np.array_equal(kb[0, g], ref[0, g]), (ctx, p, S, g)
+            else:
+                assert np.all(kb[0, g] == 0), (ctx, p, S, g)
+    # rows outside [blockBegin, blockEnd) are untouched
+    init = np.full((1, 16, 128), 0x1234, np.uint16)
+    kb = O.k_compress(full, cs, np.array([64]), w, 1e-6, 16, 5, 9, 0, dt, kbar=init)
+    assert np.all(kb[0, :5] == 0x1234) and np.all(kb[0, 9:] == 0x1234)
+    assert np.array_equal(kb[0, 5:9], ref[0, 5:9])
+
+
+def check_k1a_k1b_agree_on_constant_blocks(O):
+    """A block of four identical key rows k has mean exactly k, so its kbar equals K1a's
+    numerics applied to k with the K gamma at position 4g."""
+    rng = np.random.default_rng(29)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    cs = cos_sin_table(64, 1e4)
+    for dt in ("bf16", "f16"):
+        k = _rand_bits(rng, (16, 128), dt)
+        w = _rand_bits(rng, 128, dt, 0.1)
+        x = np.zeros((1, 64, 640), np.uint16)
+        x[0, :, 512:] = np.repeat(k, 4, axis=0)
+        kb = O.k_compress(x, cs, np.array([64]), w, 1e-6, 16, 0, 16, 0, dt)
+        xq = np.zeros((1, 64, 640), np.uint16)
+        xq[0, :, :128] = np.repeat(k, 4, axis=0)
+        q = O.q_prep(xq, cs, np.array([64]), w, 1e-6, dt)
+        assert np.array_equal(kb[0], q[0, ::4, 0]), dt
+
+
+def check_subrange_union_equals_full(O):
+    """The (blockBegin, blockEnd, pastLen) triplet compresses a sub-range of a longer sequence;
+    sub-range calls that cover [0, numBlocks) reproduce one full call bit for bit."""
+    rng = np.random.default_rng(31)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    dt = "f16"
+    S, nb = 256, 64
+    cs = cos_sin_table(S, 1e4)
+    x = _rand_bits(rng, (3, S, 640), dt)
+    ctx = np.array([256, 201, 77], np.int32)
+    w = _rand_bits(rng, 128, dt, 0.1)
+    full = O.k_compress(x, cs, ctx, w, 1e-6, nb, 0, nb, 0, dt)
+    acc = np.full((3, nb, 128), 0x5555, np.uint16)
+    for bB, bE, p in [(0, 9, 0), (9, 30, 36), (30, 41, 119), (41, 64, 164)]:
+        acc = O.k_compress(np.ascontiguousarray(x[:, p:]), cs, ctx, w, 1e-6, nb, bB, bE, p, dt,
+                           kbar=acc)
+    assert np.array_equal(acc, full)
+
+
+def check_ranges_mode(O):
+    """Per-sequence triplets: equal entries reproduce scalar mode; distinct entries reproduce
+    separate one-sequence calls."""
+    rng = np.random.default_rng(37)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    dt = "bf16"
+    S, nb, B = 8, 40, 5
+    cs = cos_sin_table(4 * nb, 1e4)
+    x = _rand_bits(rng, (B, S, 640), dt)
+    w = _rand_bits(rng, 128, dt, 0.1)
+    past = np.array([8, 12, 100, 151, 4], np.int32)
+    ctx = past + np.array([8, 4, 7, 6, 1], np.int32)
+    bB = past >> 2
+    bE = (ctx + 3) >> 2
+    span = int((bE - bB).max())
+    r = O.k_compress(x, cs, ctx, w, 1e-6, nb, 0, 0, 0, dt, ranges=(past, bB, bE, span))
+    for b in range(B):
+        one = O.k_compress(x[b:b + 1], cs, ctx[b:b + 1], w, 1e-6, nb, int(bB[b]), int(bE[b]),
+                           int(past[b]), dt)
+        assert np.array_equal(r[b], one[0]), b
+    same = O.k_compress(x, cs, np.full(B, 20, np.int32), w, 1e-6, nb, 0, 0, 0, dt,
+                        ranges=(np.full(B, 8), np.full(B, 2), np.full(B, 5), 3))
+    scal = O.k_compress(x, cs, np.full(B, 20, np.int32), w, 1e-6, nb, 2, 5, 8, dt)
+    assert np.array_equal(same, scal)
+
+
+def check_thread_count_independence(O):
+    from sparse_attention_indexer_qsa_amd import workloads
+    wl = workloads.config2("bf16", S=256)
+    outs = []
+    for n in (1, 3, 8):
+        O.set_threads(n)
+        q = O.q_prep(wl.indexQk, wl.cosSin, wl.ctx, wl.wQ, wl.eps, wl.dt)
+        k = O.k_compress(wl.indexQk, wl.cosSin, wl.ctx, wl.wK, wl.eps, wl.numBlocks, 0,
+                         wl.numBlocks, 0, wl.dt)
+        outs.append((q, k))
+    O.set_threads(8)
+    for q, k in outs[1:]:
+        assert np.array_equal(q, outs[0][0]) and np.array_equal(k, outs[0][1])
+
+
+def check_numpy_rederivation(O):
+    """An independent numpy binary32 re-derivation of the definitions (tests/numpy_model.py)
+    matches the oracle bit for bit on the tiny prefill workload and a batched fp16 one."""
+    from sparse_attention_indexer_qsa_amd import workloads
+    for wl in (workloads.config1(), workloads.config2("f16", S=128)):
+        q = O.q_prep(wl.indexQk, wl.cosSin, wl.ctx, wl.wQ, wl.eps, wl.dt)
+        qn = nm.q_prep(wl.indexQk, wl.cosSin, wl.ctx, wl.wQ, wl.eps, wl.dt)
+        assert np.array_equal(q, qn), wl.name
+        k = O.k_compress(wl.indexQk, wl.cosSin, wl.ctx, wl.wK, wl.eps, wl.numBlocks, 0,
+                         wl.numBlocks, 0, wl.dt)
+        kn = nm.k_compress(wl.indexQk, wl.cosSin, wl.ctx, wl.wK, wl.eps, wl.numBlocks, wl.dt)
+        assert np.array_equal(k, kn), wl.name
+
+
+# ---------------------------------------------------------------------------- persist ----
+
+def _pool(numPages, H=2, D=384):
+    return np.full((2 * numPages, 128, H, D), 0xA5A5, np.uint16)
+
+
+def check_pool_round_trip(O):
+    """QsaIndexerPoolState addressing, checked through an independent view of the pool as a
+    [2*numPages, 128, H, D] tensor: every written cell reads back the expected bits (K-tail =
+    the raw key bits, V-tail = the dense kbar row), unused entries and out-of-range slots skip,
+    and nothing else changes."""
+    from oracle.ref import Pool
+    rng = np.random.default_rng(41)
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    dt = "bf16"
+    B, S, numPages, m = 3, 300, 12, 4
+    nb = (S + 3) // 4
+    cs = cos_sin_table(S, 1e4)
+    x = _rand_bits(rng, (B, S, 640), dt)
+    w = _rand_bits(rng, 128, dt, 0.1)
+    ctx = np.array([300, 257, 130], np.int32)
+    pt = np.stack([rng.permutation(numPages)[:B * m].reshape(B, m),
+                   rng.permutation(numPages)[:B * m].reshape(B, m) + numPages], 1).astype(np.int32)
+    pt[1, 0, 2] = -1          # K tail page of sequence 1's tokens 256.. unused
+    pt[2, 1, 0] = -1          # V page of sequence 2's first 32 blocks unused
+    pt[0, 1, 1] = 2 * numPages + 5   # out of range id: skipped
+    data = _pool(numPages)
+    pool = Pool(data, pt, numPages, 256)
+    kb = O.k_compress(x, cs, ctx, w, 1e-6, nb, 0, nb, 0, dt, pool=pool)
+    O.persist(pool, x, None, ctx, nb, 0, nb, 0)
+    view = data.reshape(2 * numPages, 128, 2, 384)
+    expect = np.full_like(data, 0xA5A5)
+    ev = expect.reshape(view.shape)
+    for b in range(B):
+        c = int(ctx[b])
+        for t in range(c - c % 4, c):
+            pid = pt[b, 0, t // 128]
+            if pid >= 0:
+                ev[pid, t % 128, 0, 256:384] = x[b, t, 512:640]
+        for g in range(c // 4):
+            pid = pt[b, 1, (4 * g) // 128]
+            if 0 <= pid < 2 * numPages:
+                ev[pid, (4 * g) % 128, 0, 256:384] = kb[b, g]
+    assert np.array_equal(view, ev)
+    # persist with the dense kbar writes the same V-tails as the fused pool write
+    data2 = _pool(numPages)
+    pool2 = Pool(data2, pt, numPages, 256)
+    O.persist(pool2, x, kb, ctx, nb, 0, nb, 0)
+    assert np.array_equal(data2, data)
+
+
+def check_tail_rule_with_past(O):
+    """Raw-K tails: tokens [max(pastLen, ctx - ctx%4), ctx) inside the provided rows, copied
+    bit-unmodified; none when ctx % 4 == 0."""
+    from oracle.ref import Pool
+    rng = np.random.default_rng(43)
+    numPages, B, S = 8, 4, 4
+    x = rng.integers(0, 65536, (B, S, 640)).astype(np.uint16)
+    past = np.array([10, 13, 16, 127], np.int32)
+    new = np.array([3, 4, 4, 2], np.int32)
+    ctx = past + new
+    pt = np.stack([np.arange(B * 2).reshape(B, 2), np.arange(B * 2).reshape(B, 2) + numPages],
+                  1).astype(np.int32)
+    data = _pool(numPages)
+    pool = Pool(data, pt, numPages, 256)
+    O.persist(pool, x, None, ctx, 40, 0, 0, 0, ranges=(past, past >> 2, ctx >> 2, 1))
+    view = data.reshape(2 * numPages, 128, 2, 384)
+    written = {}
+    for b in range(B):
+        c, p = int(ctx[b]), int(past[b])
+        for t in range(max(p, c - c % 4), c):
+            written[(int(pt[b, 0, t // 128]), t % 128)] = x[b, t - p, 512:]
+    # 10+3=13: token 12; 13+4=17: token 16; 16+4=20: none; 127+2=129: token 128
+    assert len(written) == 3
+    for (pid, row), bits in written.items():
+        assert np.array_equal(view[pid, row, 0, 256:], bits)
+    assert np.count_nonzero(data != 0xA5A5) == np.count_nonzero(
+        np.stack(list(written.values())) != 0xA5A5)
+
+
+ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

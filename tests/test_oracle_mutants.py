@@ -1,0 +1,71 @@
+"""The pins catch plausible mistakes: each mutant below is a copy of the oracle with one
+planted error (built on the CPU into a temporary directory); at least one pin must fail on it.
+None of the mutants reads or writes out of bounds."""
+import os
+
+import pytest
+
+from oracle import build as obuild
+from oracle.ref import Oracle
+from tests import oracle_pins
+
+SRC = open(obuild.SRC).read()
+
+MUTANTS = {
+    "pairwise_mean": ("float s = k0 + k1;\n      s = s + k2;\n      s = s + k3;",
+                      "float s = (k0 + k1) + (k2 + k3);"),
+    "reversed_mean": ("float s = k0 + k1;\n      s = s + k2;\n      s = s + k3;",
+                      "float s = k3 + k2;\n      s = s + k1;\n      s = s + k0;"),
+    "mean_not_cast": ("m[d] = widen(mT, dt);", "m[d] = mean;"),
+    "gamma_prefolded": ("float w1 = 1.0f + widen(w[d], dt);", "float w1 = widen(w[d], dt);"),
+    "rope_sign_low": ("o[i] = a0 - b0;", "o[i] = a0 + b0;"),
+    "rope_sign_high": ("o[i + HALF_ROPE] = a1 + b1;", "o[i + HALF_ROPE] = a1 - b1;"),
+    "cos_sin_swapped": ("float c = cs[i], s = cs[HALF_ROPE + i];",
+                        "float s = cs[i], c = cs[HALF_ROPE + i];"),
+    "rope_on_wrong_half": ("for (int d = 2 * HALF_ROPE; d < DIM; ++d) o[d] = y[d];",
+                           "for (int d = 2 * HALF_ROPE; d < DIM; ++d) o[d] = y[d] * cs[0];"),
+    "mean_over_64": ("float meanSq = sumSq / 128.0f;", "float meanSq = sumSq / 64.0f;"),
+    "eps_dropped": ("float v = meanSq + eps;", "float v = meanSq;"),
+    "rope_at_g": ("cosSin + 4 * g * CS_W", "cosSin + g * CS_W"),
+    "padding_off_by_one": ("if (t >= L) {", "if (t > L) {"),
+    "no_pastlen_rule": ("if (!(t0 >= p)) return 0;", "(void)p;"),
+    "row_map_ignores_past": ("(4 * g + j - p)) * ROW + KCOL", "(4 * g + j - p + (p > 0))) * ROW + KCOL"),
+    "tail_start_wrong": ("int64_t t0 = c - c % 4;", "int64_t t0 = c - 4;"),
+    "v_tail_on_k_plane": ("int64_t off = pool_tail_offset(pool, b, 1, 4 * g);\n      if (off >= 0) memcpy(base",
+                          "int64_t off = pool_tail_offset(pool, b, 0, 4 * g);\n      if (off >= 0) memcpy(base"),
+    "headsize_dropped": ("+ 0 * p->poolHeadDim + p->headSize;", "+ 0 * p->poolHeadDim + 0;"),
+    "page_row_wrong": ("int64_t row = pos % PAGE;", "int64_t row = (pos + 1) % PAGE;"),
+    "bf16_truncates": ("if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
+                       "(void)rest;"),
+    "bf16_ties_away": ("(rest == 0x8000u && (keep & 1u))", "(rest == 0x8000u)"),
+    "f16_no_subnormal": ("int drop = (e >= -14) ? 13 : 13 + (-14 - e);",
+                         "if (e < -14) return sign;\n  int drop = 13;"),
+    "rsqrt_single": ("float inv = (float)(1.0 / sqrt((double)v));",
+                     "float inv = 1.0f / (float)sqrt((double)v) * (1.0f + 1.2e-7f);"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    src = SRC.replace(old, new)
+    path = os.path.join(mutant_dir, f"{name}.c")
+    open(path, "w").write(src)
+    lib = os.path.join(mutant_dir, f"lib_{name}.so")
+    import subprocess
+    subprocess.run(["gcc", *obuild.FLAGS, "-Wno-error", path, "-o", lib, "-lm"], check=True)
+    O = Oracle(lib)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(O)
+        except AssertionError:
+            caught.append(check.__name__)
+    O.set_threads(8)
+    assert caught, f"no pin catches mutant {name}"
