@@ -5,14 +5,12 @@ The compute lives in ``libqsa.so`` (hand-written HIP kernels behind the C ABI of
 ``sparse_attention_indexer_qsa_amd.workloads`` draws seeded synthetic inputs.  The binding is
 loaded on first use so that input generation works on machines without the library.
 """
+import importlib
+
 __all__ = ["qsa", "workloads"]
 
 
 def __getattr__(name):
-    if name == "qsa":
-        from . import qsa
-        return qsa
-    if name == "workloads":
-        from . import workloads
-        return workloads
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

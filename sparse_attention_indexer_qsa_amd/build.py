@@ -1,0 +1,52 @@
+"""Build libqsa.so: the gfx950 kernels and the C ABI of include/qsa.h.
+
+Ahead-of-time code objects for gfx950 only (no JIT).  Flags that matter for the numerics:
+-ffp-contract=off (no FMA contraction: each product is rounded before it is added), no
+fast-math, default IEEE denormal handling, and packed FP32 instructions disabled.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libqsa.so")
+ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-I", INCLUDE, "-I", CSRC]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; that is harmless
+    noise = "is not a recognized feature for this target"
+    out = "\n".join(l for l in r.stdout.splitlines() if noise not in l)
+    if out.strip():
+        print(out, file=sys.stderr)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed ({r.returncode}): {' '.join(cmd)}")
+
+
+def build(hipcc="hipcc"):
+    """Compile and link libqsa.so (always recompiles)."""
+    os.makedirs(BUILD, exist_ok=True)
+    kobj = os.path.join(BUILD, "qsa_kernels.o")
+    aobj = os.path.join(BUILD, "qsa_api.o")
+    _run([hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "qsa_kernels.hip"), "-o", kobj])
+    _run([hipcc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I",
+          os.path.join(ROCM, "include"), "-c",
+          os.path.join(CSRC, "qsa_api.cpp"), "-o", aobj])
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", kobj, aobj, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

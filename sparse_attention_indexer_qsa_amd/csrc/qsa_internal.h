@@ -1,0 +1,89 @@
+// qsa_internal.h — argument blocks and launchers shared by the ABI layer (qsa_api.cpp) and
+// the kernels (qsa_kernels.hip).  Not part of the public ABI; see include/qsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+enum class Dt : int { F16 = 0, BF16 = 1 };
+
+// Pool addressing of the page's QsaIndexerPoolState, pre-digested on the host.
+struct PoolArgs {
+  void* base;               // T [2*numPages, 128, H, D]
+  const int32_t* pageTable; // int32 [B, 2, maxPagesPerSeq]
+  int32_t maxPagesPerSeq;
+  int32_t numIds;           // 2*numPages: valid ids are [0, numIds)
+  int64_t rowElems;         // H*D: elements per pool row
+  int32_t headSize;         // first indexer column (head 0)
+};
+
+// Per-sequence block triplet source: scalars, or three device arrays.
+struct Ranges {
+  int32_t blockBegin, blockEnd, pastLen;  // scalar mode
+  const int32_t* pastLens;                // non-null: ranges mode
+  const int32_t* blockBegins;
+  const int32_t* blockEnds;
+  int32_t span;                           // blocks per sequence the grid covers
+};
+
+struct QPrepArgs {
+  void* qNormed;
+  const void* indexQk;
+  const float* cosSin;
+  const int32_t* ctx;
+  const void* wQ;
+  float eps;
+  int32_t B, S;
+  float* dMeanSq;  // debug outputs (debug kernels only)
+  float* dInv;
+  float* dPre;
+};
+
+struct KCompressArgs {
+  void* kbar;
+  const void* indexQk;
+  const float* cosSin;
+  int32_t maxPositions;
+  const int32_t* ctx;
+  const void* wK;
+  float eps;
+  int32_t B, S, numBlocks;
+  Ranges r;
+  PoolArgs pool;  // base == nullptr: no V-tail write
+  void* dMT;      // debug outputs (debug kernels only)
+  float* dMeanSq;
+  float* dInv;
+  float* dPre;
+};
+
+struct PersistArgs {
+  PoolArgs pool;
+  const void* indexQk;
+  const void* kbar;  // nullptr: raw-K tails only
+  const int32_t* ctx;
+  int32_t B, S, numBlocks;
+  Ranges r;
+};
+
+struct PrefillArgs {
+  void* qNormed;
+  void* kbar;
+  const void* indexQk;
+  const float* cosSin;
+  const int32_t* ctx;
+  const void* wQ;
+  const void* wK;
+  float eps;
+  int32_t B, S, numBlocks;
+  PoolArgs pool;  // base == nullptr: no pool writes
+};
+
+// Launchers: enqueue on `stream`, return the launch status.  Arguments are already validated.
+hipError_t launch_q_prep(const QPrepArgs& a, Dt dt, bool debug, hipStream_t stream);
+hipError_t launch_k_compress(const KCompressArgs& a, Dt dt, bool debug, hipStream_t stream);
+hipError_t launch_persist(const PersistArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, Dt dt, hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,197 @@
+"""The C ABI library on the host: it loads, exports every function include/qsa.h declares,
+reports its version, and rejects every invalid argument with the documented code before any
+launch.  The invalid-argument calls hand the library host addresses that are never
+dereferenced; on a machine with a GPU they are skipped (the GPU suite covers the same checks
+with device tensors)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = open(os.path.join(ROOT, "include", "qsa.h")).read()
+
+
+def _declared_functions():
+    body = re.sub(r"/\*.*?\*/", "", HEADER, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(qsa_\w+)\s*\(", body, re.M)))
+
+
+def _header_int(name):
+    m = re.search(rf"\b{name}\s*=\s*(-?\d+)", HEADER) or \
+        re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", HEADER)
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def qsa():
+    from sparse_attention_indexer_qsa_amd import qsa
+    return qsa
+
+
+def test_every_declared_symbol_is_exported(qsa):
+    names = _declared_functions()
+    assert set(names) >= {"qsa_index_q_prep", "qsa_index_k_compress", "qsa_index_persist",
+                          "qsa_index_prefill", "qsa_last_error", "qsa_abi_version"}
+    lib = ctypes.CDLL(qsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_codes(qsa):
+    assert qsa.qsa_abi_version() == _header_int("QSA_ABI_VERSION")
+    for n in ("QSA_OK", "QSA_E_INVALID", "QSA_E_ALIGN", "QSA_E_DTYPE", "QSA_E_LAUNCH",
+              "QSA_F16", "QSA_BF16"):
+        assert getattr(qsa, n) == _header_int(n), n
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+class _Host:
+    """Aligned host buffers whose addresses stand in for device pointers (never used)."""
+
+    def __init__(self):
+        self.buf = np.zeros(1 << 16, np.uint8)
+        base = self.buf.ctypes.data
+        self.a = base + (-base) % 256          # 256-byte aligned
+
+    def p(self, k=0, mis=0):
+        return self.a + 1024 * k + mis
+
+
+@pytest.fixture
+def host(qsa):
+    if _gpu_visible():
+        pytest.skip("host stand-in pointers are only used where no GPU is visible")
+    return _Host()
+
+
+def _qprep(qsa, h, **kw):
+    a = dict(q=h.p(0), x=h.p(1), cs=h.p(2), P=64, ctx=h.p(3), w=h.p(4), eps=1e-6, B=2, S=64,
+             dt=qsa.QSA_BF16)
+    a.update(kw)
+    return qsa.lib.qsa_index_q_prep(a["q"], a["x"], a["cs"], a["P"], a["ctx"], a["w"], a["eps"],
+                                    a["B"], a["S"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), "QSA_E_DTYPE"), (dict(B=-1), "QSA_E_INVALID"), (dict(S=-4), "QSA_E_INVALID"),
+    (dict(q=None), "QSA_E_INVALID"), (dict(x=None), "QSA_E_INVALID"),
+    (dict(cs=None), "QSA_E_INVALID"), (dict(ctx=None), "QSA_E_INVALID"),
+    (dict(w=None), "QSA_E_INVALID"), (dict(mis_q=2), "QSA_E_ALIGN"),
+    (dict(mis_x=8), "QSA_E_ALIGN"), (dict(mis_cs=4), "QSA_E_ALIGN"),
+    (dict(mis_ctx=2), "QSA_E_ALIGN"), (dict(mis_w=2), "QSA_E_ALIGN"),
+    (dict(P=63), "QSA_E_INVALID"), (dict(eps=float("nan")), "QSA_E_INVALID"),
+    (dict(eps=-1e-6), "QSA_E_INVALID"), (dict(eps=math.inf), "QSA_E_INVALID"),
+    (dict(B=0, q=None, x=None), "QSA_OK"), (dict(S=0, cs=None), "QSA_OK"),
+])
+def test_q_prep_validation(qsa, host, kw, code):
+    for k in list(kw):
+        if k.startswith("mis_"):
+            name = k[4:]
+            kw[name] = host.p(["q", "x", "cs", "ctx", "w"].index(name), kw.pop(k))
+    assert _qprep(qsa, host, **kw) == getattr(qsa, code)
+    if code != "QSA_OK":
+        assert qsa.qsa_last_error()
+
+
+def _pool(qsa, h, **kw):
+    a = dict(poolPtr=h.p(5), pageTable=h.p(6), maxPagesPerSeq=4, numPages=16, numKVHeads=2,
+             poolHeadDim=384, headSize=256)
+    a.update(kw)
+    return qsa.qsa_pool_state_t(a["poolPtr"], a["pageTable"], a["maxPagesPerSeq"],
+                                a["numPages"], a["numKVHeads"], a["poolHeadDim"], a["headSize"])
+
+
+def _kcomp(qsa, h, pool=None, ranges=None, **kw):
+    a = dict(kb=h.p(0), x=h.p(1), cs=h.p(2), P=64, ctx=h.p(3), w=h.p(4), eps=1e-6, B=2, S=64,
+             nb=16, bB=0, bE=16, p=0, dt=qsa.QSA_BF16)
+    a.update(kw)
+    return qsa.lib.qsa_index_k_compress(
+        a["kb"], a["x"], a["cs"], a["P"], a["ctx"], a["w"], a["eps"], a["B"], a["S"], a["nb"],
+        a["bB"], a["bE"], a["p"], None if ranges is None else ctypes.byref(ranges),
+        None if pool is None else ctypes.byref(pool), a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=-1), "QSA_E_DTYPE"), (dict(bB=5, bE=4), "QSA_E_INVALID"),
+    (dict(bE=17), "QSA_E_INVALID"), (dict(bB=-1), "QSA_E_INVALID"),
+    (dict(p=-1), "QSA_E_INVALID"), (dict(nb=-1, bE=0), "QSA_E_INVALID"),
+    (dict(P=60), "QSA_E_INVALID"), (dict(P=61), "QSA_OK_IF_NO_GPU"),
+    (dict(kb=None), "QSA_E_INVALID"), (dict(kb=1024 + 8), "QSA_E_ALIGN"),
+    (dict(eps=float("nan")), "QSA_E_INVALID"),
+    (dict(bB=3, bE=3, kb=None, x=None), "QSA_OK"), (dict(B=0, kb=None), "QSA_OK"),
+])
+def test_k_compress_validation(qsa, host, kw, code):
+    rc = _kcomp(qsa, host, **kw)
+    if code == "QSA_OK_IF_NO_GPU":
+        # maxPositions = 4*blockEnd - 3 passes validation; with no GPU the launch itself fails
+        assert rc == qsa.QSA_E_LAUNCH
+    else:
+        assert rc == getattr(qsa, code)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(numPages=0), "QSA_E_INVALID"), (dict(maxPagesPerSeq=0), "QSA_E_INVALID"),
+    (dict(numKVHeads=0), "QSA_E_INVALID"), (dict(headSize=257), "QSA_E_INVALID"),
+    (dict(headSize=-8), "QSA_E_INVALID"), (dict(headSize=252), "QSA_E_ALIGN"),
+    (dict(poolHeadDim=387, headSize=256), "QSA_E_ALIGN"),
+    (dict(numKVHeads=1, poolHeadDim=390), "QSA_E_ALIGN"),
+    (dict(poolPtr=None), "QSA_E_INVALID"), (dict(pageTable=None), "QSA_E_INVALID"),
+    (dict(poolPtr=8), "QSA_E_ALIGN"), (dict(numPages=2**30), "QSA_E_INVALID"),
+])
+def test_pool_validation(qsa, host, kw, code):
+    for k in ("poolPtr", "pageTable"):
+        if k in kw and kw[k] is not None:
+            kw[k] = host.p(5) + kw[k]
+    rc = _kcomp(qsa, host, pool=_pool(qsa, host, **kw))
+    assert rc == getattr(qsa, code)
+    rc = qsa.lib.qsa_index_persist(ctypes.byref(_pool(qsa, host, **kw)), host.p(1), None,
+                                   host.p(3), 2, 64, 16, 0, 16, 0, None, qsa.QSA_BF16, None)
+    assert rc == getattr(qsa, code)
+
+
+def test_ranges_validation(qsa, host):
+    r = qsa.qsa_seq_ranges_t(host.p(7), host.p(8), None, 1)
+    assert _kcomp(qsa, host, ranges=r) == qsa.QSA_E_INVALID
+    r = qsa.qsa_seq_ranges_t(host.p(7), host.p(8), host.p(9), -1)
+    assert _kcomp(qsa, host, ranges=r) == qsa.QSA_E_INVALID
+    r = qsa.qsa_seq_ranges_t(host.p(7), host.p(8), host.p(9, 2), 1)
+    assert _kcomp(qsa, host, ranges=r) == qsa.QSA_E_ALIGN
+    r = qsa.qsa_seq_ranges_t(host.p(7), host.p(8), host.p(9), 0)
+    # scalars are ignored in ranges mode, so a bad scalar triplet does not matter
+    assert _kcomp(qsa, host, ranges=r, bB=9, bE=2, kb=None) == qsa.QSA_OK
+
+
+def test_persist_and_prefill_validation(qsa, host):
+    L = qsa.lib
+    assert L.qsa_index_persist(None, host.p(1), None, host.p(3), 2, 64, 16, 0, 16, 0, None,
+                               qsa.QSA_BF16, None) == qsa.QSA_E_INVALID
+    assert L.qsa_index_persist(ctypes.byref(_pool(qsa, host)), host.p(1), None, host.p(3), 2, 0,
+                               16, 0, 16, 0, None, qsa.QSA_BF16, None) == qsa.QSA_OK
+    assert L.qsa_index_persist(ctypes.byref(_pool(qsa, host)), host.p(1), host.p(2, 4),
+                               host.p(3), 2, 64, 16, 0, 16, 0, None, qsa.QSA_BF16,
+                               None) == qsa.QSA_E_ALIGN
+
+    def pre(**kw):
+        a = dict(q=host.p(0), kb=host.p(1), x=host.p(2), cs=host.p(3), P=64, ctx=host.p(4),
+                 wq=host.p(5), wk=host.p(6), eps=1e-6, pool=None, B=2, S=64, nb=16,
+                 dt=qsa.QSA_F16)
+        a.update(kw)
+        return L.qsa_index_prefill(a["q"], a["kb"], a["x"], a["cs"], a["P"], a["ctx"], a["wq"],
+                                   a["wk"], a["eps"], a["pool"], a["B"], a["S"], a["nb"],
+                                   a["dt"], None)
+    assert pre(nb=15) == qsa.QSA_E_INVALID
+    assert pre(S=61, nb=15) == qsa.QSA_E_INVALID         # ceilDiv(61, 4) = 16 > 15
+    assert pre(S=60, nb=15) == qsa.QSA_E_LAUNCH          # valid; with no GPU the launch fails
+    assert pre(P=63) == qsa.QSA_E_INVALID
+    assert pre(wk=None) == qsa.QSA_E_INVALID
+    assert pre(dt=2) == qsa.QSA_E_DTYPE
+    assert pre(B=0, q=None) == qsa.QSA_OK
+    assert "maxPositions" in (pre(P=10) and qsa.qsa_last_error())
