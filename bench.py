@@ -1,0 +1,303 @@
+"""Benchmark of the QSA indexer hot path on one MI355X.
+
+A step is one pass of the whole path (index-Q norm + rope, index-K block compression, kbar
+V-tail and raw-K tail persistence) over the long single-sequence prefill workload: B = 1,
+S = 131072 tokens, T = bf16, rope theta 1e6, pool of 1024 + 1024 pages.  It is one launch of
+qsa_index_prefill through the C ABI.  The three-call sequence (qsa_index_q_prep,
+qsa_index_k_compress with the pool, qsa_index_persist) is timed beside it.
+
+Inputs are seeded synthetic data already resident in HBM.  Steps rotate over --sets copies of
+every buffer, so no step finds its inputs in the 256 MB Infinity Cache.
+
+Prints one JSON line: rows/s (value), ms per step, the roofline of the kernel (algorithmic
+bytes per launch / average launch time from HIP events recorded on the launch stream, against
+the 8 TB/s HBM peak), HBM traffic measured by rocprofv3 counters when a committed profile of
+the current kernel source exists, and the CPU oracle timed on the host's cores.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer rows/s and achieved HBM GB/s (% of peak), bf16, QPrep+KCompress+persist"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "sparse_attention_indexer_qsa_amd", "csrc", "qsa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_kernel_long_prefill.json")
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(wl):
+    """Bytes the fused prefill must move for workload `wl` (each consumed input byte once, each
+    output byte once): valid q rows, distinct cosSin rows, every qNormed row (zeros included),
+    raw keys of valid blocks, every dense kbar row of the range, the raw-K tails (read +
+    write), kbar V-tails, the page-table entries those writes read, weights and lengths."""
+    import numpy as np
+    S, B = wl.S, wl.B
+    L = np.clip(wl.ctx.astype(np.int64), 0, S)
+    k1a = 1024 * int(L.sum()) + 256 * int(L.max()) + 1024 * B * S
+    valid_blocks = L // 4
+    k1b = 1024 * int(valid_blocks.sum()) + 256 * B * wl.numBlocks
+    tails = L % 4
+    pt = wl.pool.pageTable
+    v_pages = sum(len(set(range(0, int(v) * 4, 128))) for v in valid_blocks) if len(L) else 0
+    k_pages = int((tails > 0).sum())
+    persist = 512 * int(tails.sum()) + 256 * int(valid_blocks.sum()) + 4 * (v_pages + k_pages)
+    del pt
+    return k1a + k1b + persist + 2 * 256 + 4 * B
+
+
+def survey_bytes(wl):
+    """The same count with the cosSin rows of block positions counted again for K1b (once
+    per call that consumes them, as for the three-call sequence)."""
+    import numpy as np
+    L = np.clip(wl.ctx.astype(np.int64), 0, wl.S)
+    return algorithmic_bytes(wl) + 256 * int((L // 4).max())
+
+
+def cpu_baseline(wl, reps):
+    """The oracle (plain C, OpenMP) on the host: the whole path on the same inputs."""
+    import numpy as np
+    from oracle.ref import Pool, default
+    O = default()
+    threads = O.max_threads()
+    pool = Pool(np.full(wl.pool.shape, 0xA5A5, np.uint16), wl.pool.pageTable, wl.pool.numPages,
+                wl.pool.headSize)
+
+    def run():
+        O.q_prep(wl.indexQk, wl.cosSin, wl.ctx, wl.wQ, wl.eps, wl.dt)
+        O.k_compress(wl.indexQk, wl.cosSin, wl.ctx, wl.wK, wl.eps, wl.numBlocks, 0, wl.numBlocks,
+                     0, wl.dt, pool=pool)
+        O.persist(pool, wl.indexQk, None, wl.ctx, wl.numBlocks, 0, wl.numBlocks, 0)
+
+    run()  # warm-up
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[len(times) // 2]
+    return {"value": wl.B * wl.S / t, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole long-prefill workload (B={wl.B}, S={wl.S}) through the oracle's "
+                      f"q_prep + k_compress(pool) + persist, median of {reps} runs after 1 "
+                      f"warm-up, {threads} OpenMP threads; {t * 1e3:.1f} ms per pass"}
+
+
+COPY_BYTES = 256 << 20
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    assert files, f"no *{suffix} under {d}"
+    return [r for f in files for r in csv.DictReader(open(f))]
+
+
+def _counter(d, name):
+    """Mean value of counter `name` per dispatch, by kernel name (rocprofv3 --pmc output)."""
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] == name:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize(trace_dir, fetch_dir, write_dir):
+    """profiles/ summary of the fused prefill kernel: per-kernel durations from the kernel
+    trace, HBM bytes from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
+    the same counter reads for a plain 256 MiB device copy."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    fetch, write = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        assert ks, (key, list(d))
+        return d[ks[0]][0]
+
+    copy_key = "MulFunctor"   # torch.mul over 256 MiB of float32 (--copy-calib)
+    f_scale = COPY_BYTES / (pick(fetch, copy_key) * 1024)
+    w_scale = COPY_BYTES / (pick(write, copy_key) * 1024)
+    fb = pick(fetch, "prefill_kernel") * 1024 * f_scale
+    wb = pick(write, "prefill_kernel") * 1024 * w_scale
+    rec = {"kernel": "prefill_kernel<Bf16, pool> on the long-prefill workload",
+           "kernel_source_sha256_16": kernel_source_hash(), "fetch_bytes_per_launch": fb,
+           "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
+           "fetch_scale_from_copy": f_scale, "write_scale_from_copy": w_scale}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    lines = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    print("\n".join(lines))
+    print(json.dumps(rec, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-three-call", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summary and traffic record from rocprofv3 output "
+                         "(kernel trace, FETCH_SIZE run, WRITE_SIZE run) and exit")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): the indexer hot path needs no exchange between GPUs, and this build "
+              f"runs and reports a single GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_qsa_amd.qsa as qsa
+    from sparse_attention_indexer_qsa_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    print("[bench] generating the long-prefill workload", file=sys.stderr, flush=True)
+    wl = W.config3()
+    B, S, nb = wl.B, wl.S, wl.numBlocks
+    dt = qsa.QSA_BF16
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    wQ, wK = bits(wl.wQ), bits(wl.wK)
+    host_x = torch.from_numpy(wl.indexQk.view(np.int16))
+    host_cs = torch.from_numpy(wl.cosSin)
+    sets = []
+    for i in range(args.sets):
+        x = host_x.cuda()
+        cs = host_cs.cuda()
+        ctx = torch.from_numpy(wl.ctx).cuda()
+        pt = torch.from_numpy(wl.pool.pageTable).cuda()
+        pool = torch.full(wl.pool.shape, 0xA5A5 - 65536, dtype=torch.int16, device="cuda")
+        q = torch.empty(B, S, 4, 128, dtype=torch.int16, device="cuda")
+        kb = torch.empty(B, nb, 128, dtype=torch.int16, device="cuda")
+        ps = qsa.PoolState(pool, pt, wl.pool.numPages, wl.pool.numKVHeads, wl.pool.poolHeadDim,
+                           wl.pool.headSize)
+        sets.append(dict(x=x, cs=cs, ctx=ctx, pool=ps, q=q, kb=kb, pstruct=ps.c_struct(B)))
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    L = qsa.lib
+
+    # arguments are marshalled once per buffer set; the timed loop only calls the C ABI
+    def fused_args(s):
+        return (s["q"].data_ptr(), s["kb"].data_ptr(), s["x"].data_ptr(), s["cs"].data_ptr(),
+                S, s["ctx"].data_ptr(), wQ.data_ptr(), wK.data_ptr(), wl.eps,
+                ctypes.byref(s["pstruct"]), B, S, nb, dt, sh)
+
+    fa = [fused_args(s) for s in sets]
+
+    def three_calls(s):
+        rc = L.qsa_index_q_prep(s["q"].data_ptr(), s["x"].data_ptr(), s["cs"].data_ptr(), S,
+                                s["ctx"].data_ptr(), wQ.data_ptr(), wl.eps, B, S, dt, sh)
+        rc |= L.qsa_index_k_compress(s["kb"].data_ptr(), s["x"].data_ptr(), s["cs"].data_ptr(), S,
+                                     s["ctx"].data_ptr(), wK.data_ptr(), wl.eps, B, S, nb, 0, nb,
+                                     0, None, ctypes.byref(s["pstruct"]), dt, sh)
+        rc |= L.qsa_index_persist(ctypes.byref(s["pstruct"]), s["x"].data_ptr(), None,
+                                  s["ctx"].data_ptr(), B, S, nb, 0, nb, 0, None, dt, sh)
+        return rc
+
+    torch.cuda.synchronize()
+
+    def timed(fn, steps, warmup):
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                assert fn(i % args.sets) == 0, qsa.qsa_last_error()
+            torch.cuda.synchronize()          # barrier (one rank) + device sync
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for i in range(steps):
+                fn(i % args.sets)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        return (t1 - t0) / steps, e0.elapsed_time(e1) / 1e3 / steps
+
+    print("[bench] timing the fused prefill", file=sys.stderr, flush=True)
+    wall, ev = timed(lambda i: L.qsa_index_prefill(*fa[i]), args.steps, args.warmup)
+    # per-launch distribution (events around each launch, same stream)
+    per = []
+    with torch.cuda.stream(stream):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(args.steps, 100))]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            L.qsa_index_prefill(*fa[i % args.sets])
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    three = None
+    if not args.no_three_call:
+        print("[bench] timing the three-call sequence", file=sys.stderr, flush=True)
+        w3, e3 = timed(lambda i: three_calls(sets[i]), args.steps, args.warmup)
+        three = {"ms_per_step": w3 * 1e3, "event_ms_per_step": e3 * 1e3,
+                 "rows_per_s": B * S / w3, "GBps_alg": survey_bytes(wl) / e3 / 1e9}
+    if args.copy_calib:
+        # a plain streaming kernel of known traffic: reads COPY_BYTES, writes COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+
+    alg = algorithmic_bytes(wl)
+    achieved = alg / ev / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_source_sha256_16") == kernel_source_hash():
+            traffic = t["bytes_per_launch"]
+    out = {
+        "metric": METRIC, "value": B * S / wall, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "long_prefill", "B": B, "S": S, "T": "bf16", "theta": 1e6,
+                   "numBlocks": nb, "numPages": wl.pool.numPages, "entry": "qsa_index_prefill",
+                   "buffer_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "kernel": {"name": "prefill_kernel<Bf16, pool>", "alg_bytes_per_launch": alg,
+                   "event_us_per_launch": ev * 1e6,
+                   "us_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2],
+                                      per[(9 * len(per)) // 10]],
+                   "GBps_vs_three_call_bytes": survey_bytes(wl) / ev / 1e9,
+                   "source_sha256_16": kernel_source_hash()},
+        "three_call": three,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,21 +6,23 @@
 // QsaIndexerPoolState.  How it is computed here is our own wave64 design:
 //
 //  * The unit of work is a 128-element vector (an index-Q head, a raw key, a block mean) held by
-//    one 16-lane DPP row: lane c of the row owns elements [8c, 8c+8), loaded and stored with one
-//    16-byte access.  A wave therefore carries four such vectors side by side: the four q heads
-//    of one token in K1a, four blocks in the stand-alone K1b.
-//  * Sum of squares: eight in-lane terms, then a four-step DPP butterfly (quad_perm [1,0,3,2],
-//    quad_perm [2,3,0,1], row_half_mirror, row_mirror).  Each step adds a lane's value to its
-//    mirror's, and IEEE addition is commutative, so all 16 lanes end with the same bits.
-//  * Rope partner (dims i and i+32 live in lanes c and c^4): two DPP moves (row_shl:4 into
-//    bank 0, row_shr:4 into bank 1).
+//    one 16-lane DPP row.  Lane c of the row owns elements [4c, 4c+4) and [64+4c, 64+4c+4),
+//    each moved with one 8-byte access (a row moves two full 128-byte lines per instruction).
+//    With this split every lane holds four rope elements: lanes 0..7 hold dims i < 32 and
+//    lanes 8..15 their partners i + 32, so the rope partner is lane c ^ 8, one symmetric DPP
+//    move (row_ror:8), and all 16 lanes share the rope arithmetic.  A wave carries four such
+//    vectors side by side: the four q heads of one token in K1a, four blocks in the
+//    stand-alone K1b.
+//  * Sum of squares in FP32: eight in-lane terms, then a four-step DPP butterfly (quad_perm
+//    [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror).  Each step adds a lane's
+//    value to its mirror's, and IEEE addition is commutative, so all 16 lanes end with the same
+//    bits.  The reciprocal square root is v_rsq_f32.  (The method fixes FP32 and a warp-level
+//    reduction but not its order, nor how rsqrt is rounded.)
 //  * cosSin: the 64-float row of a position is staged once in LDS per wave, together with the
-//    negated sines, and read by the rope lanes of all four rows.  With -sin stored,
+//    negated sines, and read by all four rows.  With -sin stored,
 //    o = y*cos + partner*(+-sin) covers both halves of each pair with one add (a - b and
 //    a + (-b) are the same IEEE operation).
-//  * FP32 arithmetic, no FMA contraction (-ffp-contract=off), one rounding per operation.  The
-//    sum of squares and the reciprocal square root are carried in FP64 and rounded once to
-//    FP32, which is where FP32 evaluation orders differ least from the exact value.
+//  * FP32 arithmetic, no FMA contraction (-ffp-contract=off), one rounding per operation.
 //  * Casts to T use the gfx950 packed converts (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), which
 //    round to nearest even with subnormals kept.
 //  * Rows past the context length and invalid blocks are stored as zeros without loading
@@ -52,23 +54,40 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ element conversions ---
 
-__device__ __forceinline__ void widen8(Bf16, const uint4& r, float (&f)[8]) {
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
+// The lane's share of a 128-element vector: elements [4c, 4c+4) in `a`, [64+4c, 64+4c+4) in `b`.
+struct Piece {
+  uint2 a, b;
+};
+
+__device__ __forceinline__ Piece load_piece(const void* base, int64_t vec, int c) {
+  const uint16_t* p = static_cast<const uint16_t*>(base) + vec + 4 * c;
+  return Piece{*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 64)};
 }
 
-__device__ __forceinline__ void widen8(F16, const uint4& r, float (&f)[8]) {
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
-    f[2 * i] = (float)h.x;
-    f[2 * i + 1] = (float)h.y;
-  }
+// Outputs are written once and not read again by this path: non-temporal stores keep them from
+// displacing the input stream in the caches.
+__device__ __forceinline__ void store_piece(void* base, int64_t vec, int c, const Piece& v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  uint16_t* p = static_cast<uint16_t*>(base) + vec + 4 * c;
+  __builtin_nontemporal_store(u32x2{v.a.x, v.a.y}, reinterpret_cast<u32x2*>(p));
+  __builtin_nontemporal_store(u32x2{v.b.x, v.b.y}, reinterpret_cast<u32x2*>(p + 64));
+}
+
+__device__ __forceinline__ Piece zero_piece() { return Piece{make_uint2(0, 0), make_uint2(0, 0)}; }
+
+__device__ __forceinline__ void widen4(Bf16, const uint2& r, float (&f)[4]) {
+  f[0] = __uint_as_float(r.x << 16);
+  f[1] = __uint_as_float(r.x & 0xffff0000u);
+  f[2] = __uint_as_float(r.y << 16);
+  f[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void widen4(F16, const uint2& r, float (&f)[4]) {
+  const f16x2 lo = __builtin_bit_cast(f16x2, r.x), hi = __builtin_bit_cast(f16x2, r.y);
+  f[0] = (float)lo.x;
+  f[1] = (float)lo.y;
+  f[2] = (float)hi.x;
+  f[3] = (float)hi.y;
 }
 
 __device__ __forceinline__ uint32_t pack2(Bf16, float a, float b) {
@@ -82,40 +101,29 @@ __device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
 }
 
 template <class T>
-__device__ __forceinline__ uint4 narrow8(const float (&o)[8]) {
-  return make_uint4(pack2(T{}, o[0], o[1]), pack2(T{}, o[2], o[3]), pack2(T{}, o[4], o[5]),
-                    pack2(T{}, o[6], o[7]));
+__device__ __forceinline__ uint2 narrow4(const float (&o)[4]) {
+  return make_uint2(pack2(T{}, o[0], o[1]), pack2(T{}, o[2], o[3]));
 }
 
 // ---------------------------------------------------------------------- cross-lane ops ---
 
 template <int kCtrl>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
-}
-
-template <int kCtrl>
-__device__ __forceinline__ double dpp_d(double v) {
-  const int2 p = __builtin_bit_cast(int2, v);
-  return __builtin_bit_cast(double, make_int2(dpp_i<kCtrl>(p.x), dpp_i<kCtrl>(p.y)));
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
 }
 
 // Sum over the 16 lanes of a DPP row; every lane of the row returns the same bits.
-__device__ __forceinline__ double row_sum16(double s) {
-  s = s + dpp_d<0xB1>(s);   // quad_perm [1,0,3,2]
-  s = s + dpp_d<0x4E>(s);   // quad_perm [2,3,0,1]
-  s = s + dpp_d<0x141>(s);  // row_half_mirror
-  s = s + dpp_d<0x140>(s);  // row_mirror
+__device__ __forceinline__ float row_sum16(float s) {
+  s = s + dpp_f<0xB1>(s);   // quad_perm [1,0,3,2]
+  s = s + dpp_f<0x4E>(s);   // quad_perm [2,3,0,1]
+  s = s + dpp_f<0x141>(s);  // row_half_mirror
+  s = s + dpp_f<0x140>(s);  // row_mirror
   return s;
 }
 
-// Value of lane c^4 for lanes c < 8 of each row (the rope partner); lanes c >= 8 keep v.
-__device__ __forceinline__ float partner4(float v) {
-  const int x = __builtin_bit_cast(int, v);
-  int r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x1, false);  // bank 0 <- lane + 4
-  r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0x2, false);      // bank 1 <- lane - 4
-  return __builtin_bit_cast(float, r);
-}
+// Value held by lane c ^ 8 of the same row (row_ror:8): the rope partner.
+__device__ __forceinline__ float partner8(float v) { return dpp_f<0x128>(v); }
 
 // LDS written by a wave and read back by other lanes of the same wave: LDS executes a wave's
 // operations in order, so only the compiler must be kept from reordering them.
@@ -125,10 +133,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Stage the 16-byte piece c of a cosSin row into an LDS row of kCsLds floats (and the
-// negated sines next to it).
-__device__ __forceinline__ void stage_cos_sin(float* lds_row, const float* cs_row, int c) {
-  const float4 v = *reinterpret_cast<const float4*>(cs_row + 4 * c);
+// Stage the 16-byte piece c of a cosSin row (floats [4c, 4c+4)) into an LDS row of kCsLds
+// floats, and the negated sines next to it.
+__device__ __forceinline__ void stage_cos_sin(float* lds_row, const float4& v, int c) {
   *reinterpret_cast<float4*>(lds_row + 4 * c) = v;
   if (c >= 8)
     *reinterpret_cast<float4*>(lds_row + 64 + 4 * (c - 8)) = make_float4(-v.x, -v.y, -v.z, -v.w);
@@ -139,57 +146,68 @@ __device__ __forceinline__ void stage_cos_sin(float* lds_row, const float* cs_ro
 struct RowDbg {  // debug destinations of one vector (null when not requested)
   float* meanSq;
   float* inv;
-  float* pre;    // the lane's 8 pre-cast values
+  float* pre;    // the vector's 128 pre-cast values
 };
+
+struct Gamma {   // 1 + w for the lane's 8 elements
+  float a[4], b[4];
+};
+
+template <class T>
+__device__ __forceinline__ Gamma load_gamma(const void* w, int c) {
+  const Piece r = load_piece(w, 0, c);
+  Gamma g;
+  widen4(T{}, r.a, g.a);
+  widen4(T{}, r.b, g.b);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    g.a[k] = 1.0f + g.a[k];
+    g.b[k] = 1.0f + g.b[k];
+  }
+  return g;
+}
 
 // Gemma RMSNorm with (1 + w), neox rope on dims [0, 64), cast to T, for the 128-vector held
 // by this lane's DPP row ("Qsa Indexer Kernels", launchQsaIndexQPrep "Exact numerics").
-// x: the lane's 8 values; w1 = 1 + w for them; cs: LDS cosSin row of the rope position.
+// xa/xb: the lane's values of dims [4c, 4c+4) and [64+4c, 64+4c+4); cs: LDS cosSin row of the
+// rope position.
 template <class T, bool kDbg>
-__device__ __forceinline__ uint4 norm_rope(const float (&x)[8], const float (&w1)[8], float eps,
-                                           const float* cs, int c, RowDbg dbg) {
-  double ss = 0.0;
+__device__ __forceinline__ Piece norm_rope(const float (&xa)[4], const float (&xb)[4],
+                                           const Gamma& w1, float eps, const float* cs, int c,
+                                           RowDbg dbg) {
+  float ss = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ss += (double)x[k] * (double)x[k];  // products exact in FP64
+  for (int k = 0; k < 4; ++k) ss = __builtin_fmaf(xa[k], xa[k], ss);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ss = __builtin_fmaf(xb[k], xb[k], ss);
   ss = row_sum16(ss);
-  const float meanSq = (float)ss * (1.0f / 128.0f);
-  const float v = meanSq + eps;
-  const float inv = (float)(1.0 / __builtin_sqrt((double)v));
-  float y[8], o[8];
+  const float meanSq = ss * (1.0f / 128.0f);
+  const float inv = __builtin_amdgcn_rsqf(meanSq + eps);
+  float ya[4], oa[4], ob[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    y[k] = (x[k] * inv) * w1[k];
-    o[k] = y[k];
+  for (int k = 0; k < 4; ++k) {
+    ya[k] = (xa[k] * inv) * w1.a[k];
+    ob[k] = (xb[k] * inv) * w1.b[k];
   }
-  float yp[8];
+  // lanes 0..7 hold dims i < 32 and use -sin; lanes 8..15 hold dims i + 32 and use +sin
+  const float4 cv = *reinterpret_cast<const float4*>(cs + 4 * (c & 7));
+  const float4 sv = *reinterpret_cast<const float4*>(cs + (c < 8 ? 64 : 32) + 4 * (c & 7));
+  const float cc[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-  for (int k = 0; k < 8; ++k) yp[k] = partner4(y[k]);
-  if (c < 8) {
-    // lanes 0..3 hold dims i < 32 (use -sin); lanes 4..7 hold dims i + 32 (use +sin)
-    const float* cp = cs + 8 * (c & 3);
-    const float* sp = cs + (c < 4 ? 64 : 32) + 8 * (c & 3);
-    const float4 c0 = *reinterpret_cast<const float4*>(cp);
-    const float4 c1 = *reinterpret_cast<const float4*>(cp + 4);
-    const float4 s0 = *reinterpret_cast<const float4*>(sp);
-    const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
-    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float a = y[k] * cv[k];
-      const float b = yp[k] * sv[k];
-      o[k] = a + b;
-    }
+  for (int k = 0; k < 4; ++k) {
+    const float a = ya[k] * cc[k];
+    const float b = partner8(ya[k]) * sn[k];
+    oa[k] = a + b;
   }
   if constexpr (kDbg) {
     if (c == 0) {
       *dbg.meanSq = meanSq;
       *dbg.inv = inv;
     }
-    *reinterpret_cast<float4*>(dbg.pre) = make_float4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<float4*>(dbg.pre + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    *reinterpret_cast<float4*>(dbg.pre + 4 * c) = make_float4(oa[0], oa[1], oa[2], oa[3]);
+    *reinterpret_cast<float4*>(dbg.pre + 64 + 4 * c) = make_float4(ob[0], ob[1], ob[2], ob[3]);
   }
-  return narrow8<T>(o);
+  return Piece{narrow4<T>(oa), narrow4<T>(ob)};
 }
 
 template <bool kDbg>
@@ -199,62 +217,51 @@ __device__ __forceinline__ void zero_dbg(RowDbg dbg, int c) {
       *dbg.meanSq = 0.0f;
       *dbg.inv = 0.0f;
     }
-    *reinterpret_cast<float4*>(dbg.pre) = make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(dbg.pre + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dbg.pre + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dbg.pre + 64 + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
+// Fixed-order block mean ("Qsa Indexer Kernels", launchQsaIndexKCompress) of four raw keys:
+// s = ((k0 + k1) + k2) + k3, mean = s * 0.25, cast to T (returned) and widened back (ma, mb).
 template <class T>
-__device__ __forceinline__ void load_w1(const void* w, int c, float (&w1)[8]) {
-  const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + 8 * c);
-  widen8(T{}, r, w1);
+__device__ __forceinline__ Piece block_mean(const Piece (&k)[4], float (&ma)[4],
+                                            float (&mb)[4]) {
+  float ka[4][4], kb[4][4], sa[4], sb[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) w1[k] = 1.0f + w1[k];
-}
-
-// Fixed-order block mean ("Qsa Indexer Kernels", launchQsaIndexKCompress):
-// s = ((k0 + k1) + k2) + k3, mean = s * 0.25, cast to T (returned packed) and widened back.
-template <class T>
-__device__ __forceinline__ uint4 block_mean(const uint4& r0, const uint4& r1, const uint4& r2,
-                                            const uint4& r3, float (&m)[8]) {
-  float k0[8], k1[8], k2[8], k3[8], mean[8];
-  widen8(T{}, r0, k0);
-  widen8(T{}, r1, k1);
-  widen8(T{}, r2, k2);
-  widen8(T{}, r3, k3);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float s = k0[k] + k1[k];
-    s = s + k2[k];
-    s = s + k3[k];
-    mean[k] = s * 0.25f;
+  for (int j = 0; j < 4; ++j) {
+    widen4(T{}, k[j].a, ka[j]);
+    widen4(T{}, k[j].b, kb[j]);
   }
-  const uint4 mT = narrow8<T>(mean);
-  widen8(T{}, mT, m);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float s = ka[0][e] + ka[1][e];
+    s = s + ka[2][e];
+    s = s + ka[3][e];
+    sa[e] = s * 0.25f;
+    float t = kb[0][e] + kb[1][e];
+    t = t + kb[2][e];
+    t = t + kb[3][e];
+    sb[e] = t * 0.25f;
+  }
+  const Piece mT{narrow4<T>(sa), narrow4<T>(sb)};
+  widen4(T{}, mT.a, ma);
+  widen4(T{}, mT.b, mb);
   return mT;
 }
 
 // ---------------------------------------------------------------------- pool addressing ---
 
-// Element offset of column headSize + 8c of the tail row of `pos` in `plane` for sequence b,
-// or -1 when the slot is outside [0, maxPagesPerSeq) or the entry is -1 or outside
-// [0, 2*numPages) (QsaIndexerPoolState: guarded before any dereference).
+// Element offset of column headSize of the tail row of `pos` in `plane` for sequence b, or -1
+// when the slot is outside [0, maxPagesPerSeq) or the entry is -1 or outside [0, 2*numPages)
+// (QsaIndexerPoolState: guarded before any dereference).
 __device__ __forceinline__ int64_t tail_offset(const PoolArgs& p, int64_t b, int plane,
-                                               int64_t pos, int c) {
+                                               int64_t pos) {
   const int64_t slot = pos >> 7;
   if (slot < 0 || slot >= p.maxPagesPerSeq) return -1;
   const int32_t id = p.pageTable[(b * 2 + plane) * p.maxPagesPerSeq + slot];
   if (id < 0 || id >= p.numIds) return -1;
-  return ((int64_t)id * kPageTokens + (pos & (kPageTokens - 1))) * p.rowElems + p.headSize +
-         8 * c;
-}
-
-__device__ __forceinline__ void store16(void* base, int64_t elem_off, const uint4& v) {
-  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + elem_off) = v;
-}
-
-__device__ __forceinline__ uint4 load16(const void* base, int64_t elem_off) {
-  return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+  return ((int64_t)id * kPageTokens + (pos & (kPageTokens - 1))) * p.rowElems + p.headSize;
 }
 
 __device__ __forceinline__ int32_t clamp_len(int32_t ctx, int32_t S) {
@@ -272,34 +279,36 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(QPrepArgs a, int32_t w
   const int32_t b = blockIdx.x / wgPerSeq;
   const int64_t t0 = ((int64_t)(blockIdx.x - b * wgPerSeq) * kWaves + wave) * 4;
   if (t0 >= a.S) return;
+  const Gamma w1 = load_gamma<T>(a.wQ, c);
   const int32_t L = clamp_len(a.ctx[b], a.S);
   const int64_t row0 = (int64_t)b * a.S + t0;
 
-  uint4 raw[4];
+  float4 csv;
+  if (t0 + h < L) csv = *reinterpret_cast<const float4*>(a.cosSin + (t0 + h) * kCsW + 4 * c);
+  Piece raw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (t0 + j < L) raw[j] = load16(a.indexQk, (row0 + j) * kRow + h * kDim + 8 * c);
-  if (t0 + h < L) stage_cos_sin(cs_lds[wave][h], a.cosSin + (t0 + h) * kCsW, c);
-  float w1[8];
-  load_w1<T>(a.wQ, c, w1);
+    if (t0 + j < L) raw[j] = load_piece(a.indexQk, (row0 + j) * kRow + h * kDim, c);
+  if (t0 + h < L) stage_cos_sin(cs_lds[wave][h], csv, c);
   wave_lds_sync();
 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (t0 + j >= a.S) break;
-    const int64_t qoff = (row0 + j) * kQElems + h * kDim + 8 * c;
+    const int64_t qvec = (row0 + j) * kQElems + h * kDim;
     RowDbg dbg{};
     if constexpr (kDbg) {
       dbg.meanSq = a.dMeanSq + (row0 + j) * 4 + h;
       dbg.inv = a.dInv + (row0 + j) * 4 + h;
-      dbg.pre = a.dPre + qoff;
+      dbg.pre = a.dPre + qvec;
     }
     if (t0 + j < L) {
-      float x[8];
-      widen8(T{}, raw[j], x);
-      store16(a.qNormed, qoff, norm_rope<T, kDbg>(x, w1, a.eps, cs_lds[wave][j], c, dbg));
+      float xa[4], xb[4];
+      widen4(T{}, raw[j].a, xa);
+      widen4(T{}, raw[j].b, xb);
+      store_piece(a.qNormed, qvec, c, norm_rope<T, kDbg>(xa, xb, w1, a.eps, cs_lds[wave][j], c, dbg));
     } else {
-      store16(a.qNormed, qoff, make_uint4(0, 0, 0, 0));
+      store_piece(a.qNormed, qvec, c, zero_piece());
       zero_dbg<kDbg>(dbg, c);
     }
   }
@@ -326,6 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_kernel(KCompressArgs a,
     bE = a.r.blockEnd;
     p = a.r.pastLen;
   }
+  const Gamma w1 = load_gamma<T>(a.wK, c);
   const int64_t g = bB + i;
   const bool inRange = i < a.r.span && g < bE && g >= 0 && g < a.numBlocks;
   const int64_t t0 = 4 * g;
@@ -333,15 +343,14 @@ __global__ __launch_bounds__(kThreads) void k_compress_kernel(KCompressArgs a,
   const bool valid = inRange && t0 + 3 < ctx && t0 >= p && t0 + 3 - p < a.S &&
                      t0 < a.maxPositions;
 
-  uint4 kr[4];
+  Piece kr[4];
   if (valid) {
-    const int64_t src = ((int64_t)b * a.S + (t0 - p)) * kRow + kKCol + 8 * c;
+    const int64_t src = ((int64_t)b * a.S + (t0 - p)) * kRow + kKCol;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kr[j] = load16(a.indexQk, src + j * kRow);
-    stage_cos_sin(cs_lds[wave][r], a.cosSin + t0 * kCsW, c);
+    for (int j = 0; j < 4; ++j) kr[j] = load_piece(a.indexQk, src + j * kRow, c);
+    stage_cos_sin(cs_lds[wave][r], *reinterpret_cast<const float4*>(a.cosSin + t0 * kCsW + 4 * c),
+                  c);
   }
-  float w1[8];
-  load_w1<T>(a.wK, c, w1);
   wave_lds_sync();
   if (!inRange) return;
 
@@ -350,21 +359,21 @@ __global__ __launch_bounds__(kThreads) void k_compress_kernel(KCompressArgs a,
   if constexpr (kDbg) {
     dbg.meanSq = a.dMeanSq + o;
     dbg.inv = a.dInv + o;
-    dbg.pre = a.dPre + o * kDim + 8 * c;
+    dbg.pre = a.dPre + o * kDim;
   }
   if (valid) {
-    float m[8];
-    const uint4 mT = block_mean<T>(kr[0], kr[1], kr[2], kr[3], m);
-    if constexpr (kDbg) store16(a.dMT, o * kDim + 8 * c, mT);
-    const uint4 out = norm_rope<T, kDbg>(m, w1, a.eps, cs_lds[wave][r], c, dbg);
-    store16(a.kbar, o * kDim + 8 * c, out);
+    float ma[4], mb[4];
+    const Piece mT = block_mean<T>(kr, ma, mb);
+    if constexpr (kDbg) store_piece(a.dMT, o * kDim, c, mT);
+    const Piece out = norm_rope<T, kDbg>(ma, mb, w1, a.eps, cs_lds[wave][r], c, dbg);
+    store_piece(a.kbar, o * kDim, c, out);
     if constexpr (kPool) {
-      const int64_t off = tail_offset(a.pool, b, 1, t0, c);
-      if (off >= 0) store16(a.pool.base, off, out);
+      const int64_t off = tail_offset(a.pool, b, 1, t0);
+      if (off >= 0) store_piece(a.pool.base, off, c, out);
     }
   } else {
-    store16(a.kbar, o * kDim + 8 * c, make_uint4(0, 0, 0, 0));
-    if constexpr (kDbg) store16(a.dMT, o * kDim + 8 * c, make_uint4(0, 0, 0, 0));
+    store_piece(a.kbar, o * kDim, c, zero_piece());
+    if constexpr (kDbg) store_piece(a.dMT, o * kDim, c, zero_piece());
     zero_dbg<kDbg>(dbg, c);
   }
 }
@@ -396,17 +405,17 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs a, int32_
     if (t < p) t = p;
     t += item;
     if (t >= ctx || t - p < 0 || t - p >= a.S) return;
-    const int64_t off = tail_offset(a.pool, b, 0, t, c);
+    const int64_t off = tail_offset(a.pool, b, 0, t);
     if (off < 0) return;
-    store16(a.pool.base, off,
-            load16(a.indexQk, ((int64_t)b * a.S + (t - p)) * kRow + kKCol + 8 * c));
+    store_piece(a.pool.base, off, c,
+                load_piece(a.indexQk, ((int64_t)b * a.S + (t - p)) * kRow + kKCol, c));
   } else if constexpr (kKbar) {
     const int64_t i = item - kTailSlots, g = bB + i, t0 = 4 * g;
     if (!(i < a.r.span && g < bE && g >= 0 && g < a.numBlocks)) return;
     if (!(t0 + 3 < ctx && t0 >= p && t0 + 3 - p < a.S)) return;
-    const int64_t off = tail_offset(a.pool, b, 1, t0, c);
+    const int64_t off = tail_offset(a.pool, b, 1, t0);
     if (off < 0) return;
-    store16(a.pool.base, off, load16(a.kbar, ((int64_t)b * a.numBlocks + g) * kDim + 8 * c));
+    store_piece(a.pool.base, off, c, load_piece(a.kbar, ((int64_t)b * a.numBlocks + g) * kDim, c));
   }
 }
 
@@ -414,72 +423,94 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs a, int32_
 // One wave per 4-token block g of one sequence: K1a for its 4 tokens (row h = q head h),
 // K1b for the block, the kbar V-tail, and the raw-K tails of an incomplete last block.  Every
 // indexQk row and cosSin row is read once.
+//
+// A block whose four tokens are all inside the context takes a straight-line path: every load
+// is issued up front in the order the data is consumed (gammas, the cosSin row and raw key of
+// token t0 + h in row h, then the four q rows), so each wait covers only what is needed next.
+// Boundary and padding blocks take a per-token path that reads only valid rows.
+
+template <class T>
+__device__ __forceinline__ Piece q_token(const Piece& raw, const Gamma& w1, float eps,
+                                         const float* cs, int c) {
+  float xa[4], xb[4];
+  widen4(T{}, raw.a, xa);
+  widen4(T{}, raw.b, xb);
+  return norm_rope<T, false>(xa, xb, w1, eps, cs, c, RowDbg{});
+}
 
 template <class T, bool kPool>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_t wgPerSeq) {
   __shared__ float cs_lds[kWaves][4][kCsLds];
-  __shared__ uint4 k_lds[kWaves][4][16];
+  __shared__ Piece k_lds[kWaves][4][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 4, c = lane & 15;
   const int32_t b = blockIdx.x / wgPerSeq;
   const int64_t g = (int64_t)(blockIdx.x - b * wgPerSeq) * kWaves + wave;
   const int64_t t0 = 4 * g;
   if (t0 >= a.S) return;
+  const Gamma w1q = load_gamma<T>(a.wQ, c);
+  const Gamma w1k = load_gamma<T>(a.wK, c);
   const int32_t L = clamp_len(a.ctx[b], a.S);
   const int64_t row0 = (int64_t)b * a.S + t0;
+  const int64_t kvec = ((int64_t)b * a.numBlocks + g) * kDim;
 
-  uint4 raw[4];
+  if (t0 + 3 < L) {
+    // ---- full block
+    const float4 csv = *reinterpret_cast<const float4*>(a.cosSin + (t0 + h) * kCsW + 4 * c);
+    const Piece key = load_piece(a.indexQk, (row0 + h) * kRow + kKCol, c);
+    Piece raw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = load_piece(a.indexQk, (row0 + j) * kRow + h * kDim, c);
+    stage_cos_sin(cs_lds[wave][h], csv, c);
+    k_lds[wave][h][c] = key;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      store_piece(a.qNormed, (row0 + j) * kQElems + h * kDim, c,
+                  q_token<T>(raw[j], w1q, a.eps, cs_lds[wave][j], c));
+    // every row computes the block (identical bits); row 0 stores it
+    const Piece kk[4] = {k_lds[wave][0][c], k_lds[wave][1][c], k_lds[wave][2][c],
+                         k_lds[wave][3][c]};
+    float ma[4], mb[4];
+    block_mean<T>(kk, ma, mb);
+    const Piece out = norm_rope<T, false>(ma, mb, w1k, a.eps, cs_lds[wave][0], c, RowDbg{});
+    if (h == 0) {
+      store_piece(a.kbar, kvec, c, out);
+      if constexpr (kPool) {
+        const int64_t off = tail_offset(a.pool, b, 1, t0);
+        if (off >= 0) store_piece(a.pool.base, off, c, out);
+      }
+    }
+    return;
+  }
+
+  // ---- boundary or padding block: the kbar row is zero; tokens below L are K1a rows and,
+  // since their block is incomplete, raw-K tails
+  const bool tokValid = t0 + h < L;
+  Piece raw[4], key;
+  if (tokValid) {
+    const float4 csv = *reinterpret_cast<const float4*>(a.cosSin + (t0 + h) * kCsW + 4 * c);
+    key = load_piece(a.indexQk, (row0 + h) * kRow + kKCol, c);
+    stage_cos_sin(cs_lds[wave][h], csv, c);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (t0 + j < L) raw[j] = load16(a.indexQk, (row0 + j) * kRow + h * kDim + 8 * c);
-  // row h also fetches the raw key of token t0 + h and stages the cosSin row of t0 + h
-  const bool tokValid = t0 + h < L;
-  uint4 key;
-  if (tokValid) {
-    key = load16(a.indexQk, (row0 + h) * kRow + kKCol + 8 * c);
-    stage_cos_sin(cs_lds[wave][h], a.cosSin + (t0 + h) * kCsW, c);
-  }
-  float w1q[8], w1k[8];
-  load_w1<T>(a.wQ, c, w1q);
-  load_w1<T>(a.wK, c, w1k);
-  const bool blockValid = t0 + 3 < L;
-  if (blockValid) k_lds[wave][h][c] = key;
+    if (t0 + j < L) raw[j] = load_piece(a.indexQk, (row0 + j) * kRow + h * kDim, c);
   wave_lds_sync();
-
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (t0 + j >= a.S) break;
-    const int64_t qoff = (row0 + j) * kQElems + h * kDim + 8 * c;
-    if (t0 + j < L) {
-      float x[8];
-      widen8(T{}, raw[j], x);
-      store16(a.qNormed, qoff, norm_rope<T, false>(x, w1q, a.eps, cs_lds[wave][j], c, RowDbg{}));
-    } else {
-      store16(a.qNormed, qoff, make_uint4(0, 0, 0, 0));
-    }
+    const int64_t qvec = (row0 + j) * kQElems + h * kDim;
+    if (t0 + j < L)
+      store_piece(a.qNormed, qvec, c, q_token<T>(raw[j], w1q, a.eps, cs_lds[wave][j], c));
+    else
+      store_piece(a.qNormed, qvec, c, zero_piece());
   }
-
-  const int64_t kout = ((int64_t)b * a.numBlocks + g) * kDim + 8 * c;
-  if (blockValid) {
-    // every row computes the block (identical bits); row 0 stores it
-    float m[8];
-    block_mean<T>(k_lds[wave][0][c], k_lds[wave][1][c], k_lds[wave][2][c], k_lds[wave][3][c], m);
-    const uint4 out = norm_rope<T, false>(m, w1k, a.eps, cs_lds[wave][0], c, RowDbg{});
-    if (h == 0) {
-      store16(a.kbar, kout, out);
-      if constexpr (kPool) {
-        const int64_t off = tail_offset(a.pool, b, 1, t0, c);
-        if (off >= 0) store16(a.pool.base, off, out);
-      }
-    }
-  } else {
-    if (h == 0) store16(a.kbar, kout, make_uint4(0, 0, 0, 0));
-    if constexpr (kPool) {
-      // tokens of an incomplete block below L are the raw-K tail: copy them bit-unmodified
-      if (tokValid) {
-        const int64_t off = tail_offset(a.pool, b, 0, t0 + h, c);
-        if (off >= 0) store16(a.pool.base, off, key);
-      }
+  if (h == 0) store_piece(a.kbar, kvec, c, zero_piece());
+  if constexpr (kPool) {
+    if (tokValid) {
+      const int64_t off = tail_offset(a.pool, b, 0, t0 + h);
+      if (off >= 0) store_piece(a.pool.base, off, c, key);
     }
   }
 }
