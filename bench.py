@@ -112,10 +112,22 @@ def _counter(d, name):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+PROFILE_MD = os.path.join(ROOT, "profiles", "prefill_kernel_long_prefill.md")
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/ptrace -o run -- "
+             "python3 $R/bench.py --steps 50 --warmup 10 --no-cpu",
+    "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pfetch -o run "
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --copy-calib",
+    "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pwrite -o run "
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --copy-calib",
+}
+
+
 def summarize(trace_dir, fetch_dir, write_dir):
     """profiles/ summary of the fused prefill kernel: per-kernel durations from the kernel
     trace, HBM bytes from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
-    the same counter reads for a plain 256 MiB device copy."""
+    the same counter reads for a plain 256 MiB streaming kernel (torch.mul, --copy-calib)."""
+    from sparse_attention_indexer_qsa_amd import workloads as W
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     fetch, write = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
 
@@ -125,22 +137,48 @@ def summarize(trace_dir, fetch_dir, write_dir):
         return d[ks[0]][0]
 
     copy_key = "MulFunctor"   # torch.mul over 256 MiB of float32 (--copy-calib)
-    f_scale = COPY_BYTES / (pick(fetch, copy_key) * 1024)
-    w_scale = COPY_BYTES / (pick(write, copy_key) * 1024)
-    fb = pick(fetch, "prefill_kernel") * 1024 * f_scale
-    wb = pick(write, "prefill_kernel") * 1024 * w_scale
+    f_copy, w_copy = pick(fetch, copy_key), pick(write, copy_key)
+    f_scale, w_scale = COPY_BYTES / (f_copy * 1024), COPY_BYTES / (w_copy * 1024)
+    f_k, w_k = pick(fetch, "prefill_kernel"), pick(write, "prefill_kernel")
+    fb, wb = f_k * 1024 * f_scale, w_k * 1024 * w_scale
+    alg = algorithmic_bytes(W.config3())
     rec = {"kernel": "prefill_kernel<Bf16, pool> on the long-prefill workload",
            "kernel_source_sha256_16": kernel_source_hash(), "fetch_bytes_per_launch": fb,
            "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
            "fetch_scale_from_copy": f_scale, "write_scale_from_copy": w_scale}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
-    lines = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    pre = [r for r in stats if "prefill_kernel" in r["Name"]][0]
+    avg_us = float(pre["AverageNs"]) / 1e3
+    md = [f"# prefill_kernel (fused K1a + K1b + persist) — long prefill, B=1, S=131072, bf16", "",
+          f"Kernel source hash (first 16 hex of sha256 of `qsa_kernels.hip`): "
+          f"`{kernel_source_hash()}`.  MI355X (gfx950), one GPU.",
+          f"Algorithmic bytes per launch: {alg:,}.", "", "## Kernel durations", "",
+          "Command (run from `/tmp` with `TMPDIR=/tmp`; `R` is the repository root):", "",
+          "    " + PROFILE_CMDS["trace"], "",
+          "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    print("\n".join(lines))
-    print(json.dumps(rec, indent=1))
+        name = r["Name"].replace("qsa::(anonymous namespace)::", "").split("(")[0]
+        md.append(f"| `{name[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    md += ["", f"Fused kernel: {alg:,} B / {avg_us:.2f} us = {alg / avg_us / 1e6:.2f} TB/s = "
+           f"{100 * alg / avg_us / 1e6 / 8:.1f} % of the 8 TB/s HBM peak.", "",
+           "## HBM traffic (counters)", "",
+           "One counter per run; each run includes `torch.mul` over 256 MiB of float32, a "
+           "reference kernel that reads and writes 268,435,456 B:", "",
+           "    " + PROFILE_CMDS["fetch"], "    " + PROFILE_CMDS["write"], "",
+           "| counter (KiB per dispatch) | reference kernel | scale | prefill_kernel | bytes |",
+           "|---|---|---|---|---|",
+           f"| FETCH_SIZE | {f_copy:,.0f} (for 262,144 read) | x {f_scale:.3f} | {f_k:,.0f} | "
+           f"{fb:,.0f} |",
+           f"| WRITE_SIZE | {w_copy:,.0f} (for 262,144 written) | x {w_scale:.3f} | {w_k:,.0f} | "
+           f"{wb:,.0f} |", "",
+           f"Measured {fb + wb:,.0f} B per launch against {alg:,} algorithmic "
+           f"({100 * (fb + wb - alg) / alg:+.2f} %).", "",
+           "Written by `python bench.py --summarize gpurun_out/ptrace gpurun_out/pfetch "
+           "gpurun_out/pwrite` (also writes `traffic_prefill_kernel_long_prefill.json`)."]
+    open(PROFILE_MD, "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 
 def main():
