@@ -220,6 +220,30 @@ static void triplet(int64_t b, int32_t bB, int32_t bE, int32_t pl, const int32_t
 }
 
 /*
+ * K1b numerics of one block from its four raw keys ("Qsa Indexer Kernels",
+ * launchQsaIndexKCompress; reused verbatim by launchQsaIndexerPreDecode): per dim d,
+ * s = ((k0+k1)+k2)+k3 in binary32 in that order, mean = s * 0.25, m_T = T(mean),
+ * m = f32(m_T); then norm_rope(m) with wK and the cosSin row `cs` of the block's position.
+ */
+static void compress_block(const uint16_t* const k[RATIO], const uint16_t* wK, const float* cs,
+                           float eps, int dt, uint16_t* out, uint16_t* dbgMT, float* dbgMeanSq,
+                           float* dbgInv, float* dbgPre) {
+  float m[DIM];
+  for (int d = 0; d < DIM; ++d) {
+    float k0 = widen(k[0][d], dt), k1 = widen(k[1][d], dt);
+    float k2 = widen(k[2][d], dt), k3 = widen(k[3][d], dt);
+    float s = k0 + k1;
+    s = s + k2;
+    s = s + k3;
+    float mean = s * 0.25f;
+    uint16_t mT = narrow(mean, dt);
+    if (dbgMT) dbgMT[d] = mT;
+    m[d] = widen(mT, dt);
+  }
+  norm_rope(m, wK, cs, eps, dt, out, dbgMeanSq, dbgInv, dbgPre);
+}
+
+/*
  * launchQsaIndexKCompress validity: the block is complete and fully inside the provided rows,
  * 4g+3 < ctx and 4g >= pastLen; "inside the provided rows" also bounds the last row,
  * 4g+3-pastLen < S; and the rope row 4g must exist in cosSin (checkMaxPos).
@@ -270,20 +294,9 @@ void ref_k_compress(uint16_t* kbar, const uint16_t* indexQk, const float* cosSin
     }
     const uint16_t* k[RATIO];
     for (int j = 0; j < RATIO; ++j) k[j] = indexQk + ((b * S) + (4 * g + j - p)) * ROW + KCOL;
-    float m[DIM];
-    for (int d = 0; d < DIM; ++d) {
-      float k0 = widen(k[0][d], dt), k1 = widen(k[1][d], dt);
-      float k2 = widen(k[2][d], dt), k3 = widen(k[3][d], dt);
-      float s = k0 + k1;
-      s = s + k2;
-      s = s + k3;
-      float mean = s * 0.25f;
-      uint16_t mT = narrow(mean, dt);
-      if (dbgMT) dbgMT[o * DIM + d] = mT;
-      m[d] = widen(mT, dt);
-    }
-    norm_rope(m, wK, cosSin + 4 * g * CS_W, eps, dt, out, dbgMeanSq ? dbgMeanSq + o : 0,
-              dbgInv ? dbgInv + o : 0, dbgPre ? dbgPre + o * DIM : 0);
+    compress_block(k, wK, cosSin + 4 * g * CS_W, eps, dt, out, dbgMT ? dbgMT + o * DIM : 0,
+                   dbgMeanSq ? dbgMeanSq + o : 0, dbgInv ? dbgInv + o : 0,
+                   dbgPre ? dbgPre + o * DIM : 0);
     if (pool) {
       int64_t off = pool_tail_offset(pool, b, 1, 4 * g);
       if (off >= 0) memcpy((uint16_t*)pool->poolPtr + off, out, sizeof(uint16_t) * DIM);
@@ -328,6 +341,77 @@ void ref_persist(const ref_pool_t* pool, const uint16_t* indexQk, const uint16_t
       if (!block_valid(g, c, p, S, 0, 0)) continue;
       int64_t off = pool_tail_offset(pool, b, 1, 4 * g);
       if (off >= 0) memcpy(base + off, kbar + (b * numBlocks + g) * DIM, sizeof(uint16_t) * DIM);
+    }
+  }
+}
+
+/* ----------------------------------------------------------------- decode pre-pass ---- */
+
+/*
+ * launchQsaIndexerPreDecode, with n new tokens per sequence (newLens[b]; NULL means the page's
+ * single token).  ctx[b] is the TOTAL length including the new tokens, so they are positions
+ * p .. ctx-1 with p = ctx - n, held in indexQk rows 0 .. n-1 of [B, S, 640] (n <= S; n is also
+ * capped at ctx).
+ *  1. K1a numerics at each new token's position -> qNormed[b, j] ([B, S, 4, 128]); rows j >= n
+ *     are +0.  ctx <= 0 or n <= 0 writes zeros and skips steps 2 and 3.
+ *  2. Tokens whose block stays incomplete, [max(p, ctx - ctx%4), ctx), store their raw key
+ *     bit-unmodified to their K-tail.
+ *  3. Each block completed by the new tokens, g in [floor(p/4), floor(ctx/4)): keys of tokens
+ *     below p are read from their pool K-tails, keys of new tokens from indexQk; the K1b numerics
+ *     of compress_block at position 4g; the kbar row is written to the V-tail of token 4g.  A block
+ *     whose earlier keys are not in the pool (page guard fails) is skipped.
+ * Positions at or past maxPositions are outside the cosSin table: their q rows stay +0 and their
+ * blocks are skipped.
+ */
+void ref_pre_decode(uint16_t* qNormed, const uint16_t* indexQk, const float* cosSin,
+                    int32_t maxPositions, const int32_t* ctx, const int32_t* newLens,
+                    const uint16_t* wQ, const uint16_t* wK, float eps, const ref_pool_t* pool,
+                    int32_t B, int32_t S, int dt) {
+  uint16_t* base = (uint16_t*)pool->poolPtr;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t c = ctx[b];
+    int64_t n = newLens ? newLens[b] : 1;
+    if (n > S) n = S;
+    if (n > c) n = c;
+    uint16_t* qb = qNormed + b * S * HEADS * DIM;
+    memset(qb, 0, sizeof(uint16_t) * S * HEADS * DIM);
+    if (c <= 0 || n <= 0) continue;
+    int64_t p = c - n;
+    for (int64_t j = 0; j < n; ++j) {
+      int64_t t = p + j;
+      if (t >= maxPositions) continue;
+      for (int h = 0; h < HEADS; ++h) {
+        float x[DIM];
+        for (int d = 0; d < DIM; ++d) x[d] = widen(indexQk[(b * S + j) * ROW + h * DIM + d], dt);
+        norm_rope(x, wQ, cosSin + t * CS_W, eps, dt, qb + (j * HEADS + h) * DIM, 0, 0, 0);
+      }
+    }
+    int64_t t0 = c - c % 4;
+    if (t0 < p) t0 = p;
+    for (int64_t t = t0; t < c; ++t) {
+      int64_t off = pool_tail_offset(pool, b, 0, t);
+      if (off >= 0) memcpy(base + off, indexQk + (b * S + (t - p)) * ROW + KCOL, sizeof(uint16_t) * DIM);
+    }
+    for (int64_t g = p / 4; 4 * g + 3 < c; ++g) {
+      if (4 * g >= maxPositions) continue;
+      const uint16_t* k[RATIO];
+      int ok = 1;
+      for (int j = 0; j < RATIO && ok; ++j) {
+        int64_t t = 4 * g + j;
+        if (t >= p) {
+          k[j] = indexQk + (b * S + (t - p)) * ROW + KCOL;
+        } else {
+          int64_t off = pool_tail_offset(pool, b, 0, t);
+          if (off < 0) ok = 0;
+          else k[j] = base + off;
+        }
+      }
+      if (!ok) continue;
+      uint16_t out[DIM];
+      compress_block(k, wK, cosSin + 4 * g * CS_W, eps, dt, out, 0, 0, 0, 0);
+      int64_t off = pool_tail_offset(pool, b, 1, 4 * g);
+      if (off >= 0) memcpy(base + off, out, sizeof(uint16_t) * DIM);
     }
   }
 }

@@ -86,12 +86,13 @@ class Oracle:
         L.ref_k_compress.argtypes = [P, P, P, I32, P, P, F32, I32, I32, I32, I32, I32, I32,
                                      P, P, P, I32, P, ctypes.c_int, P, P, P, P]
         L.ref_persist.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, I32]
+        L.ref_pre_decode.argtypes = [P, P, P, I32, P, P, P, P, F32, P, I32, I32, ctypes.c_int]
         L.ref_widen.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_narrow.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_set_threads.argtypes = [ctypes.c_int]
         L.ref_max_threads.restype = ctypes.c_int
         for f in (L.ref_q_prep, L.ref_k_compress, L.ref_persist, L.ref_widen, L.ref_narrow,
-                  L.ref_set_threads):
+                  L.ref_set_threads, L.ref_pre_decode):
             f.restype = None
         self.L = L
 
@@ -177,6 +178,25 @@ class Oracle:
                            blockBegin, blockEnd, pastLen, _p(pl), _p(bb), _p(be), ms)
 
 
+    def pre_decode(self, indexQk, cosSin, ctx, newLens, wQ, wK, eps, pool, dt,
+                   maxPositions=None):
+        """Decode pre-pass.  indexQk uint16 [B,S,640] holds each sequence's new tokens in rows
+        0..n-1; ctx = TOTAL lengths; newLens int32 [B] or None (one new token).  Returns
+        qNormed uint16 [B,S,4,128]; K-tails and V-tails go to `pool` in place."""
+        indexQk, wQ, wK = _u16(indexQk), _u16(wQ), _u16(wK)
+        cosSin = np.ascontiguousarray(cosSin, dtype=np.float32)
+        ctx = _i32(ctx)
+        nl = None if newLens is None else _i32(newLens)
+        B, S, W = indexQk.shape
+        assert W == 640 and ctx.shape == (B,)
+        q = np.empty((B, S, 4, 128), np.uint16)
+        ps = pool.c_struct()
+        mp = cosSin.shape[0] if maxPositions is None else int(maxPositions)
+        self.L.ref_pre_decode(_p(q), _p(indexQk), _p(cosSin), mp, _p(ctx), _p(nl), _p(wQ),
+                              _p(wK), float(eps), ctypes.byref(ps), B, S, _dt(dt))
+        return q
+
+
 _default = None
 
 
@@ -190,6 +210,6 @@ def default():
 def __getattr__(name):
     # module-level q_prep / k_compress / persist / widen / narrow / ... use the default build
     if name in ("q_prep", "k_compress", "persist", "widen", "narrow", "set_threads",
-                "max_threads"):
+                "max_threads", "pre_decode"):
         return getattr(default(), name)
     raise AttributeError(name)

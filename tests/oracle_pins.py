@@ -403,4 +403,99 @@ def check_tail_rule_with_past(O):
         np.stack(list(written.values())) != 0xA5A5)
 
 
+# ------------------------------------------------------------------- decode pre-pass ----
+
+def _history(rng, dt, lengths, numPages=None):
+    """Random full histories [B, Lmax, 640], gammas, cosSin table and a page table with
+    unique ids (V ids offset by numPages)."""
+    from sparse_attention_indexer_qsa_amd.workloads import cos_sin_table
+    B, Lmax = len(lengths), int(max(lengths))
+    m = (Lmax + 127) // 128
+    numPages = B * m if numPages is None else numPages
+    x = _rand_bits(rng, (B, Lmax, 640), dt)
+    wQ, wK = _rand_bits(rng, 128, dt, 0.1), _rand_bits(rng, 128, dt, 0.1)
+    pt = np.stack([rng.permutation(numPages)[:B * m].reshape(B, m),
+                   rng.permutation(numPages)[:B * m].reshape(B, m) + numPages], 1).astype(np.int32)
+    return x, wQ, wK, cos_sin_table(Lmax + 8, 1e4), pt, numPages
+
+
+def check_pre_decode_equals_prefill(O):
+    """launchQsaIndexerPreDecode: the raw key is stored bit-unmodified so that decode-time
+    compression is bit-identical to prefill K1b.  Prefill of a prefix, then decode steps of 1..4
+    new tokens, must leave in the V-tails exactly the kbar rows of one prefill over the whole
+    history, and give the same q rows as K1a over the whole history."""
+    from oracle.ref import Pool
+    rng = np.random.default_rng(53)
+    for dt in ("bf16", "f16"):
+        L = np.array([300, 257, 131, 9], np.int32)
+        x, wQ, wK, cs, pt, numPages = _history(rng, dt, L)
+        B, Lmax = x.shape[:2]
+        nb = (Lmax + 3) // 4
+        kb_full = O.k_compress(x, cs, L, wK, 1e-6, nb, 0, nb, 0, dt)
+        q_full = O.q_prep(x, cs, L, wQ, 1e-6, dt)
+        data = np.full((2 * numPages, 128, 2, 384), 0xA5A5, np.uint16)
+        pool = Pool(data, pt, numPages, 256)
+        p0 = np.array([37, 128, 1, 0], np.int32)
+        Spre = int(p0.max())
+        O.k_compress(np.ascontiguousarray(x[:, :Spre]), cs, p0, wK, 1e-6, nb, 0, nb, 0, dt,
+                     pool=pool)
+        O.persist(pool, np.ascontiguousarray(x[:, :Spre]), None, p0, nb, 0, nb, 0)
+        cur = p0.copy()
+        single = dt == "f16"   # the page's form: one new token per step, newLens = NULL
+        while np.any(cur < L):
+            n = np.minimum(1 if single else rng.integers(1, 5, B), L - cur).astype(np.int32)
+            rows = np.zeros((B, 4, 640), np.uint16)
+            for b in range(B):
+                rows[b, :n[b]] = x[b, cur[b]:cur[b] + n[b]]
+            ctx = (cur + n).astype(np.int32)
+            if single:
+                live = n > 0
+                q = O.pre_decode(rows[live], cs, ctx[live], None, wQ, wK, 1e-6,
+                                 Pool(data, pt[live], numPages, 256), dt)
+                qq = np.zeros((B, 4, 4, 128), np.uint16)
+                qq[live] = q
+                q = qq
+            else:
+                q = O.pre_decode(rows, cs, ctx, n, wQ, wK, 1e-6, pool, dt)
+            for b in range(B):
+                assert np.array_equal(q[b, :n[b]], q_full[b, cur[b]:ctx[b]]), (dt, b, cur[b])
+                assert np.all(q[b, n[b]:] == 0)
+            cur = ctx
+        view = data.reshape(2 * numPages, 128, 2, 384)
+        for b in range(B):
+            for g in range(int(L[b]) // 4):
+                pid = pt[b, 1, (4 * g) // 128]
+                assert np.array_equal(view[pid, (4 * g) % 128, 0, 256:], kb_full[b, g]), (dt, b, g)
+
+
+def check_pre_decode_guards(O):
+    """Lengths <= 0 write zero q rows and touch no pool cell; a K-tail page marked unused makes
+    the completed block uncomputable (no V-tail write) while its q rows are still produced; the
+    default of one new token equals newLens = 1."""
+    from oracle.ref import Pool
+    rng = np.random.default_rng(59)
+    dt = "bf16"
+    L = np.array([8, 12, 40], np.int32)
+    x, wQ, wK, cs, pt, numPages = _history(rng, dt, L)
+    rows = np.ascontiguousarray(x[:, :4])
+    data = np.full((2 * numPages, 128, 2, 384), 0xA5A5, np.uint16)
+    q = O.pre_decode(rows, cs, np.array([0, -3, 0], np.int32), None, wQ, wK, 1e-6,
+                     Pool(data, pt, numPages, 256), dt)
+    assert np.all(q == 0) and np.all(data == 0xA5A5)
+    ctx = np.array([4, 8, 12], np.int32)            # each completes a block
+    pt2 = pt.copy()
+    pt2[1, 0, 0] = -1                              # sequence 1: earlier keys not in the pool
+    q1 = O.pre_decode(rows, cs, ctx, None, wQ, wK, 1e-6, Pool(data, pt2, numPages, 256), dt)
+    view = data.reshape(2 * numPages, 128, 2, 384)
+    assert np.all(view[pt2[1, 1, 0], 4, 0, 256:] == 0xA5A5)
+    assert not np.all(q1[1, 0] == 0)
+    # exactly two cells changed: the V-tails of sequences 0 and 2 (no K-tail: blocks complete)
+    rows_written = np.unique(np.argwhere(view != 0xA5A5)[:, :2], axis=0)
+    assert len(rows_written) == 2, rows_written
+    data2 = np.full_like(data, 0xA5A5)
+    q2 = O.pre_decode(rows, cs, ctx, np.ones(3, np.int32), wQ, wK, 1e-6,
+                      Pool(data2, pt2, numPages, 256), dt)
+    assert np.array_equal(q1, q2) and np.array_equal(data, data2)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -12,10 +12,10 @@ from tests import oracle_pins
 SRC = open(obuild.SRC).read()
 
 MUTANTS = {
-    "pairwise_mean": ("float s = k0 + k1;\n      s = s + k2;\n      s = s + k3;",
+    "pairwise_mean": ("float s = k0 + k1;\n    s = s + k2;\n    s = s + k3;",
                       "float s = (k0 + k1) + (k2 + k3);"),
-    "reversed_mean": ("float s = k0 + k1;\n      s = s + k2;\n      s = s + k3;",
-                      "float s = k3 + k2;\n      s = s + k1;\n      s = s + k0;"),
+    "reversed_mean": ("float s = k0 + k1;\n    s = s + k2;\n    s = s + k3;",
+                      "float s = k3 + k2;\n    s = s + k1;\n    s = s + k0;"),
     "mean_not_cast": ("m[d] = widen(mT, dt);", "m[d] = mean;"),
     "gamma_prefolded": ("float w1 = 1.0f + widen(w[d], dt);", "float w1 = widen(w[d], dt);"),
     "rope_sign_low": ("o[i] = a0 - b0;", "o[i] = a0 + b0;"),
@@ -40,6 +40,13 @@ MUTANTS = {
     "bf16_ties_away": ("(rest == 0x8000u && (keep & 1u))", "(rest == 0x8000u)"),
     "f16_no_subnormal": ("int drop = (e >= -14) ? 13 : 13 + (-14 - e);",
                          "if (e < -14) return sign;\n  int drop = 13;"),
+    "decode_rope_position": ("norm_rope(x, wQ, cosSin + t * CS_W, eps, dt, qb",
+                             "norm_rope(x, wQ, cosSin + (t + 1) * CS_W, eps, dt, qb"),
+    "decode_first_block_skipped": ("for (int64_t g = p / 4;", "for (int64_t g = (p + 3) / 4;"),
+    "decode_tails_of_completed_blocks": ("int64_t t0 = c - c % 4;\n    if (t0 < p) t0 = p;\n    for",
+                                         "int64_t t0 = p;\n    for"),
+    "decode_past_keys_wrong_plane": ("int64_t off = pool_tail_offset(pool, b, 0, t);\n          if (off < 0) ok = 0;",
+                                     "int64_t off = pool_tail_offset(pool, b, 1, t);\n          if (off < 0) ok = 0;"),
     "rsqrt_single": ("float inv = (float)(1.0 / sqrt((double)v));",
                      "float inv = 1.0f / (float)sqrt((double)v) * (1.0f + 1.2e-7f);"),
 }
