@@ -189,6 +189,34 @@ int qsa_index_prefill(void* qNormed, void* kbar, const void* indexQk, const floa
                       void* stream);
 
 /*
+ * Decode pre-pass ("Qsa Indexer Kernels": launchQsaIndexerPreDecode), with n new tokens per
+ * sequence (the page's form has exactly one: pass newLens = NULL).
+ *
+ * qNormed  [out] T [B, S, 4, 128]: row j of sequence b is the K1a output of its new token j.
+ * indexQk  [in]  T [B, S, 640]: rows 0 .. n-1 of each sequence are its new tokens.
+ * cosSin   [in]  FP32 [maxPositions, 64]; must cover max(contextLengths).
+ * contextLengths [in] device int32 [B]: TOTAL lengths including the new tokens.
+ * newLens  [in]  device int32 [B] (n per sequence, capped at S and at the length) or NULL (1).
+ * wQ, wK   [in]  T [128] raw gammas.   pool: required.   seqLen = S >= 1 rows per sequence.
+ * With p = ctx - n (the past length), per sequence:
+ *  1. K1a numerics of each new token at its position p + j; rows j >= n are +0.
+ *     ctx <= 0 writes zeros and skips steps 2 and 3.
+ *  2. Tokens whose block stays incomplete, [max(p, ctx - ctx%4), ctx), copy their raw key
+ *     bit-unmodified to their K-tail.
+ *  3. Each block the new tokens complete, g in [floor(p/4), floor(ctx/4)): keys of tokens below
+ *     p are read from their pool K-tails, keys of new tokens from indexQk; K1b numerics at 4g;
+ *     the kbar row is written to the V-tail of token 4g (no dense kbar).  A block whose earlier
+ *     keys are not in the pool (page guard fails) is skipped.
+ * Positions at or past maxPositions produce +0 q rows and skipped blocks.  Because raw keys are
+ * persisted bit-unmodified, decode-time kbar rows equal those of a prefill over the history.
+ */
+int qsa_index_pre_decode(void* qNormed, const void* indexQk, const float* cosSin,
+                         int32_t maxPositions, const int32_t* contextLengths,
+                         const int32_t* newLens, const void* wQ, const void* wK, float rmsEps,
+                         const qsa_pool_state_t* pool, int32_t batchSize, int32_t seqLen,
+                         qsa_dtype dt, void* stream);
+
+/*
  * Debug forms: the same kernels with their FP32 intermediates written out.  Arguments as the
  * entry point of the same name, plus (all device FP32 unless noted, all required):
  *   qsa_debug_q_prep:     meanSq [B,S,4], invRms [B,S,4], preCast [B,S,4,128];

@@ -291,6 +291,36 @@ QSA_EXPORT int qsa_index_prefill(void* qNormed, void* kbar, const void* indexQk,
                   "qsa_index_prefill");
 }
 
+QSA_EXPORT int qsa_index_pre_decode(void* qNormed, const void* indexQk, const float* cosSin,
+                                    int32_t maxPositions, const int32_t* contextLengths,
+                                    const int32_t* newLens, const void* wQ, const void* wK,
+                                    float rmsEps, const qsa_pool_state_t* pool,
+                                    int32_t batchSize, int32_t seqLen, qsa_dtype dt,
+                                    void* stream) {
+  qsa::Dt t;
+  TRY(check_dt(dt, &t));
+  if (batchSize < 0 || seqLen < 1)
+    return fail(QSA_E_INVALID, "batchSize = %d, seqLen = %d (need seqLen >= 1)", batchSize,
+                seqLen);
+  if (maxPositions < 0) return fail(QSA_E_INVALID, "maxPositions = %d < 0", maxPositions);
+  if (batchSize == 0) return ok();
+  TRY(need(qNormed, "qNormed", 16));
+  TRY(need(indexQk, "indexQk", 16));
+  TRY(need(cosSin, "cosSin", 16));
+  TRY(need(contextLengths, "contextLengths", 4));
+  if (newLens != nullptr) TRY(need(newLens, "newLens", 4));
+  TRY(need(wQ, "wQ", 16));
+  TRY(need(wK, "wK", 16));
+  TRY(check_eps(rmsEps));
+  qsa::PoolArgs p{};
+  TRY(check_pool(pool, &p));
+  const qsa::PreDecodeArgs a{qNormed, indexQk, cosSin, maxPositions, contextLengths, newLens,
+                             wQ, wK, rmsEps, batchSize, seqLen, p};
+  (void)hipGetLastError();
+  return launched(qsa::launch_pre_decode(a, t, static_cast<hipStream_t>(stream)),
+                  "qsa_index_pre_decode");
+}
+
 QSA_EXPORT const char* qsa_last_error(void) { return g_err; }
 
 QSA_EXPORT int qsa_abi_version(void) { return QSA_ABI_VERSION; }

@@ -80,10 +80,25 @@ struct PrefillArgs {
   PoolArgs pool;  // base == nullptr: no pool writes
 };
 
+struct PreDecodeArgs {
+  void* qNormed;
+  const void* indexQk;
+  const float* cosSin;
+  int32_t maxPositions;
+  const int32_t* ctx;
+  const int32_t* newLens;  // nullptr: one new token per sequence
+  const void* wQ;
+  const void* wK;
+  float eps;
+  int32_t B, S;
+  PoolArgs pool;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.  Arguments are already validated.
 hipError_t launch_q_prep(const QPrepArgs& a, Dt dt, bool debug, hipStream_t stream);
 hipError_t launch_k_compress(const KCompressArgs& a, Dt dt, bool debug, hipStream_t stream);
 hipError_t launch_persist(const PersistArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, Dt dt, hipStream_t stream);
+hipError_t launch_pre_decode(const PreDecodeArgs& a, Dt dt, hipStream_t stream);
 
 }  // namespace qsa

@@ -537,6 +537,90 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
   prefill_block<T, kPool>(a, b, g, L, w1q, w1k, cs_lds[wave], k_lds[wave], h, c);
 }
 
+// ------------------------------------------------------------------ decode pre-pass ---
+// "Qsa Indexer Kernels", launchQsaIndexerPreDecode, with n new tokens per sequence (newLens;
+// the page's form is one).  One workgroup per sequence; ctx is the TOTAL length, the new
+// tokens are positions p .. ctx-1 (p = ctx - n) held in rows 0 .. n-1 of the sequence.
+//  * K1a: wave w takes rows w, w+4, ... (row h of the wave = q head h) at position p + j.
+//  * Raw-K tails: tokens [max(p, ctx - ctx%4), ctx) (their block stays incomplete), one DPP
+//    row each, bit copies.
+//  * Blocks completed by the new tokens, g in [p/4, ctx/4): DPP row R = 4*wave + r takes
+//    g = p/4 + R, + 16, ...; keys of tokens below p come from their pool K-tails (written by
+//    earlier calls), keys of new tokens from indexQk; K1b numerics; kbar to the V-tail of 4g.
+//    Tails written by this call are all at positions >= p, so no read depends on them.
+
+template <class T, bool kNewLens>
+__global__ __launch_bounds__(kThreads) void pre_decode_kernel(PreDecodeArgs a) {
+  __shared__ float cs_lds[kWaves][4][kCsLds];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int64_t b = blockIdx.x;
+  const Gamma w1q = load_gamma<T>(a.wQ, c);
+  const Gamma w1k = load_gamma<T>(a.wK, c);
+  const int64_t ctx = a.ctx[b];
+  int64_t n = kNewLens ? a.newLens[b] : 1;
+  if (n > a.S) n = a.S;
+  if (n > ctx) n = ctx;
+  const bool live = ctx > 0 && n > 0;
+  const int64_t p = ctx - n;
+  float* cs = cs_lds[wave][r];
+
+  for (int64_t j = wave; j < a.S; j += kWaves) {
+    const int64_t qvec = ((b * a.S + j) * 4 + r) * kDim;
+    const int64_t t = p + j;
+    if (live && j < n && t < a.maxPositions) {
+      const Piece raw = stream_piece(a.indexQk, (b * a.S + j) * kRow + r * kDim, c);
+      stage_cos_sin(cs, load_cs(a.cosSin + t * kCsW, c), c);
+      wave_lds_sync();
+      store_piece(a.qNormed, qvec, c, q_token<T>(raw, w1q, a.eps, cs, c));
+      wave_lds_sync();
+    } else {
+      store_piece(a.qNormed, qvec, c, zero_piece());
+    }
+  }
+  if (!live) return;
+
+  if (wave == kWaves - 1 && r < kTailSlots) {
+    int64_t t = ctx - (ctx & 3);
+    if (t < p) t = p;
+    t += r;
+    if (t < ctx) {
+      const int64_t off = tail_offset(a.pool, b, 0, t);
+      if (off >= 0)
+        store_piece(a.pool.base, off, c,
+                    stream_piece(a.indexQk, (b * a.S + (t - p)) * kRow + kKCol, c));
+    }
+  }
+
+  const int64_t gEnd = ctx >> 2;
+  for (int64_t g = (p >> 2) + 4 * wave + r; g < gEnd; g += 4 * kWaves) {
+    const int64_t t0 = 4 * g;
+    if (t0 >= a.maxPositions) continue;
+    Piece kk[4];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + j;
+      if (t >= p) {
+        kk[j] = stream_piece(a.indexQk, (b * a.S + (t - p)) * kRow + kKCol, c);
+      } else {
+        const int64_t off = tail_offset(a.pool, b, 0, t);
+        if (off < 0) ok = false;
+        else kk[j] = load_piece(a.pool.base, off, c);
+      }
+    }
+    if (!ok) continue;
+    stage_cos_sin(cs, load_cs(a.cosSin + t0 * kCsW, c), c);
+    wave_lds_sync();
+    float ma[4], mb[4];
+    block_mean<T>(kk, ma, mb);
+    const Piece out = norm_rope<T, false>(ma, mb, w1k, a.eps, cs, c, RowDbg{});
+    const int64_t off = tail_offset(a.pool, b, 1, t0);
+    if (off >= 0) store_piece(a.pool.base, off, c, out);
+    wave_lds_sync();
+  }
+}
+
 inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
 }  // namespace
@@ -607,6 +691,19 @@ hipError_t launch_prefill(const PrefillArgs& a, Dt dt, hipStream_t stream) {
   } else {
     if (pool) hipLaunchKernelGGL((prefill_kernel<F16, true>), grid, block, 0, stream, a, wgPerSeq);
     else hipLaunchKernelGGL((prefill_kernel<F16, false>), grid, block, 0, stream, a, wgPerSeq);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pre_decode(const PreDecodeArgs& a, Dt dt, hipStream_t stream) {
+  const dim3 grid((unsigned)a.B), block(kThreads);
+  const bool nl = a.newLens != nullptr;
+  if (dt == Dt::BF16) {
+    if (nl) hipLaunchKernelGGL((pre_decode_kernel<Bf16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((pre_decode_kernel<Bf16, false>), grid, block, 0, stream, a);
+  } else {
+    if (nl) hipLaunchKernelGGL((pre_decode_kernel<F16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((pre_decode_kernel<F16, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -49,6 +49,7 @@ def _declare(lib):
                                  P, P, P, P],
         "qsa_index_persist": [P, P, P, P, I, I, I, I, I, I, P, ctypes.c_int, P],
         "qsa_index_prefill": [P, P, P, P, I, P, P, P, F, P, I, I, I, ctypes.c_int, P],
+        "qsa_index_pre_decode": [P, P, P, I, P, P, P, P, F, P, I, I, ctypes.c_int, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -237,6 +238,25 @@ def qsa_index_prefill(qNormed, kbar, indexQk, cosSin, contextLengths, wQ, wK, rm
                                  _dev(wQ, "wQ", HEAD_DIM, _T), _dev(wK, "wK", HEAD_DIM, _T),
                                  float(rmsEps), _ref(ps), B, S, numBlocks, _dt_of(indexQk, dt),
                                  _stream(stream)))
+
+
+def qsa_index_pre_decode(qNormed, indexQk, cosSin, contextLengths, wQ, wK, rmsEps, pool,
+                         newLens=None, batchSize=None, seqLen=None, dt=None, stream=None):
+    """Decode pre-pass: K1a of the new tokens (rows 0..n-1 of each sequence), raw-K tails, and
+    the kbar V-tails of blocks the new tokens complete.  `newLens` int32 [B] or None (one)."""
+    B = indexQk.shape[0] if batchSize is None else batchSize
+    S = indexQk.shape[1] if seqLen is None else seqLen
+    if B == 0:
+        return
+    P = cosSin.shape[0]
+    nl = None if newLens is None else _dev(newLens, "newLens", B, _I32)
+    _check(lib.qsa_index_pre_decode(_dev(qNormed, "qNormed", B * S * HEADS * HEAD_DIM, _T),
+                                    _dev(indexQk, "indexQk", B * S * ROW_WIDTH, _T),
+                                    _dev(cosSin, "cosSin", P * 64, _F32), P,
+                                    _dev(contextLengths, "contextLengths", B, _I32), nl,
+                                    _dev(wQ, "wQ", HEAD_DIM, _T), _dev(wK, "wK", HEAD_DIM, _T),
+                                    float(rmsEps), ctypes.byref(pool.c_struct(B)), B, S,
+                                    _dt_of(indexQk, dt), _stream(stream)))
 
 
 def qsa_last_error():
