@@ -27,6 +27,7 @@
  * OpenMP splits rows and blocks over threads; every output element is written by exactly one
  * iteration, so results do not depend on the thread count.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -415,6 +416,83 @@ void ref_pre_decode(uint16_t* qNormed, const uint16_t* indexQk, const float* cos
     }
   }
 }
+
+/* ------------------------------------------------------------------- block scores ---- */
+
+/* The score scale 1/sqrtf(128), evaluated in binary32: sqrt then divide, each rounded. */
+static float score_scale(void) {
+  float r = sqrtf(128.0f);
+  return 1.0f / r;
+}
+
+/*
+ * Block relevance of one query token against one kbar row ("Qsa Indexer Kernels",
+ * launchQsaIndexScores): per head h the FP32 dot q_h . kbar (products of T values are exact;
+ * the sum, whose order the page leaves open, is taken exactly in binary64 and rounded once),
+ * ReLU per head, the four heads summed in ascending h in binary32, then scaled by 1/sqrtf(128)
+ * after the sum.
+ */
+static float block_score(const uint16_t* q, const uint16_t* kb, int dt) {
+  float sum = 0.0f;
+  for (int h = 0; h < HEADS; ++h) {
+    double acc = 0.0;
+    for (int d = 0; d < DIM; ++d) acc += (double)widen(q[h * DIM + d], dt) * (double)widen(kb[d], dt);
+    float dot = (float)acc;
+    float relu = dot > 0.0f ? dot : 0.0f;
+    sum = sum + relu;
+  }
+  return score_scale() * sum;
+}
+
+/*
+ * launchQsaIndexScores: logits [numRows, numBlocks] for the global rows r = b*S + t in
+ * [rowStart, rowStart + numRows).  A padded row (t >= ctx[b], or ctx[b] <= 0) is -FLT_MAX
+ * throughout and reads nothing; otherwise block g is visible iff g < nVis(t) = (t+1)/4 (complete
+ * blocks up to t) and gets block_score, and invisible blocks get -FLT_MAX.
+ */
+void ref_scores(float* logits, const uint16_t* qNormed, const uint16_t* kbar, const int32_t* ctx,
+                int32_t B, int32_t S, int32_t numBlocks, int32_t rowStart, int32_t numRows,
+                int dt) {
+  (void)B;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < numRows; ++i) {
+    int64_t r = rowStart + i, b = r / S, t = r % S;
+    float* out = logits + i * (int64_t)numBlocks;
+    int64_t c = ctx[b];
+    if (c <= 0 || t >= c) {
+      for (int64_t g = 0; g < numBlocks; ++g) out[g] = -FLT_MAX;
+      continue;
+    }
+    int64_t nVis = (t + 1) / 4;
+    const uint16_t* q = qNormed + r * HEADS * DIM;
+    for (int64_t g = 0; g < numBlocks; ++g)
+      out[g] = g < nVis ? block_score(q, kbar + (b * numBlocks + g) * DIM, dt) : -FLT_MAX;
+  }
+}
+
+/*
+ * launchQsaIndexScoresDecode: one query token per sequence (qNormed [B, 1, 4, 128]) against the
+ * kbar rows held in the V-tails: for g < nVis = ctx/4 (and g < maxBlocks), logits[b][g] =
+ * block_score(q_b, V-tail of token 4g).  Only that prefix is written.  A block whose V-tail
+ * page entry is unused or out of range has no kbar: it scores -FLT_MAX.
+ */
+void ref_scores_decode(float* logits, const uint16_t* qNormed, const int32_t* ctx,
+                       const ref_pool_t* pool, int32_t B, int32_t maxBlocks, int dt) {
+  const uint16_t* base = (const uint16_t*)pool->poolPtr;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t c = ctx[b];
+    int64_t nVis = c > 0 ? c / 4 : 0;
+    if (nVis > maxBlocks) nVis = maxBlocks;
+    for (int64_t g = 0; g < nVis; ++g) {
+      int64_t off = pool_tail_offset(pool, b, 1, 4 * g);
+      logits[b * maxBlocks + g] =
+          off < 0 ? -FLT_MAX : block_score(qNormed + b * HEADS * DIM, base + off, dt);
+    }
+  }
+}
+
+float ref_score_scale(void) { return score_scale(); }
 
 /* ------------------------------------------------------------------------- utilities ---- */
 

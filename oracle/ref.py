@@ -87,12 +87,15 @@ class Oracle:
                                      P, P, P, I32, P, ctypes.c_int, P, P, P, P]
         L.ref_persist.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, I32]
         L.ref_pre_decode.argtypes = [P, P, P, I32, P, P, P, P, F32, P, I32, I32, ctypes.c_int]
+        L.ref_scores.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_int]
+        L.ref_scores_decode.argtypes = [P, P, P, P, I32, I32, ctypes.c_int]
+        L.ref_score_scale.restype = ctypes.c_float
         L.ref_widen.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_narrow.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_set_threads.argtypes = [ctypes.c_int]
         L.ref_max_threads.restype = ctypes.c_int
         for f in (L.ref_q_prep, L.ref_k_compress, L.ref_persist, L.ref_widen, L.ref_narrow,
-                  L.ref_set_threads, L.ref_pre_decode):
+                  L.ref_set_threads, L.ref_pre_decode, L.ref_scores, L.ref_scores_decode):
             f.restype = None
         self.L = L
 
@@ -197,6 +200,36 @@ class Oracle:
         return q
 
 
+    def scores(self, qNormed, kbar, ctx, rowStart, numRows, dt):
+        """Block scores.  qNormed uint16 [B,S,4,128], kbar uint16 [B,numBlocks,128] ->
+        logits float32 [numRows, numBlocks] for global rows [rowStart, rowStart+numRows)."""
+        qNormed, kbar = _u16(qNormed), _u16(kbar)
+        ctx = _i32(ctx)
+        B, S = qNormed.shape[:2]
+        nb = kbar.shape[1]
+        out = np.empty((numRows, nb), np.float32)
+        self.L.ref_scores(_p(out), _p(qNormed), _p(kbar), _p(ctx), B, S, nb, rowStart, numRows,
+                          _dt(dt))
+        return out
+
+    def scores_decode(self, qNormed, ctx, pool, maxBlocks, dt, logits=None):
+        """Decode block scores from V-tails.  qNormed uint16 [B,1,4,128] (or [B,4,128]);
+        returns logits float32 [B, maxBlocks]; entries past each row's prefix keep `logits`'s
+        content (NaN when None)."""
+        qNormed = _u16(qNormed)
+        ctx = _i32(ctx)
+        B = qNormed.shape[0]
+        out = np.full((B, maxBlocks), np.nan, np.float32) if logits is None else \
+            np.ascontiguousarray(logits, np.float32).copy()
+        ps = pool.c_struct()
+        self.L.ref_scores_decode(_p(out), _p(qNormed), _p(ctx), ctypes.byref(ps), B, maxBlocks,
+                                 _dt(dt))
+        return out
+
+    def score_scale(self):
+        return self.L.ref_score_scale()
+
+
 _default = None
 
 
@@ -210,6 +243,6 @@ def default():
 def __getattr__(name):
     # module-level q_prep / k_compress / persist / widen / narrow / ... use the default build
     if name in ("q_prep", "k_compress", "persist", "widen", "narrow", "set_threads",
-                "max_threads", "pre_decode"):
+                "max_threads", "pre_decode", "scores", "scores_decode", "score_scale"):
         return getattr(default(), name)
     raise AttributeError(name)

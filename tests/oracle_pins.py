@@ -498,4 +498,142 @@ def check_pre_decode_guards(O):
     assert np.array_equal(q1, q2) and np.array_equal(data, data2)
 
 
+# ---------------------------------------------------------------------- block scores ----
+
+NEG_FLT_MAX_BITS = 0xFF7FFFFF
+
+
+def _bf16(x):
+    from sparse_attention_indexer_qsa_amd.workloads import to_bits
+    return to_bits(np.asarray(x, np.float32), "bf16")
+
+
+def check_score_scale(O):
+    """The scale 1/sqrtf(128) is the binary32 value numpy computes with float32 sqrt and
+    divide."""
+    assert np.float32(O.score_scale()) == np.float32(1) / np.sqrt(np.float32(128))
+
+
+def check_scores_closed_forms(O):
+    """launchQsaIndexScores: ReLU per head (not after the sum), heads summed, scale after the
+    sum.  One-hot q heads against a one-hot kbar row give exact head dots (a_h * b)."""
+    c = np.float32(1) / np.sqrt(np.float32(128))
+    for dots, expect_sum in [((0.5, 1.0, -2.0, -0.5), 1.5), ((3.0, 5.0, -7.0, 1.0), 9.0),
+                             ((-1.0, -2.0, -3.0, -4.0), 0.0)]:
+        q = np.zeros((1, 4, 4, 128), np.uint16)
+        kb = np.zeros((1, 1, 128), np.uint16)
+        for h, a in enumerate(dots):
+            q[0, 3, h, 7] = _bf16([a])[0]          # token 3 sees block 0
+        kb[0, 0, 7] = _bf16([1.0])[0]
+        lg = O.scores(q, kb, np.array([4]), 3, 1, "bf16")
+        assert lg[0, 0] == np.float32(expect_sum) * c, (dots, lg[0, 0])
+    # scale after the sum: head dots 2.40625 and 3.765625 (both bf16 values) round differently
+    # when scaled before summing: c*(x+y) = 0.5455218, c*x + c*y = 0.54552186
+    x, y = np.float32(2.40625), np.float32(3.765625)
+    assert np.float32(c * np.float32(x + y)) != np.float32(np.float32(c * x) + np.float32(c * y))
+    q = np.zeros((1, 4, 4, 128), np.uint16)
+    kb = np.zeros((1, 1, 128), np.uint16)
+    q[0, 3, 0, 5], q[0, 3, 1, 9] = _bf16([x])[0], _bf16([y])[0]
+    kb[0, 0, 5] = kb[0, 0, 9] = _bf16([1.0])[0]
+    lg = O.scores(q, kb, np.array([4]), 3, 1, "bf16")
+    assert lg[0, 0] == np.float32(c * np.float32(x + y))
+
+
+def check_scores_mask_and_padding(O):
+    """Invisible blocks (g >= (t+1)/4) and padded rows (t >= ctx, ctx <= 0) are exactly -FLT_MAX;
+    padded q rows and invisible kbar rows are never read (NaN there changes nothing)."""
+    rng = np.random.default_rng(67)
+    B, S = 3, 40
+    nb = S // 4
+    q = _bf16(rng.standard_normal((B, S, 4, 128)))
+    kb = _bf16(rng.standard_normal((B, nb, 128)))
+    ctx = np.array([40, 17, 0], np.int32)
+    lg = O.scores(q, kb, ctx, 0, B * S, "bf16").reshape(B, S, nb)
+    bits = lg.view(np.uint32)
+    for b in range(B):
+        for t in range(S):
+            nvis = (t + 1) // 4 if t < ctx[b] else 0
+            assert np.all(bits[b, t, nvis:] == NEG_FLT_MAX_BITS), (b, t)
+            assert np.all(np.isfinite(lg[b, t, :nvis])) and np.all(lg[b, t, :nvis] >= 0)
+    q2, kb2 = q.copy(), kb.copy()
+    q2[1, 17:] = 0x7FC0
+    q2[2] = 0x7FC0
+    kb2[1, 4:] = 0x7FC0        # t < 17 sees blocks < 4 only
+    assert np.array_equal(O.scores(q2, kb2, ctx, 0, B * S, "bf16").view(np.uint32),
+                          bits.reshape(B * S, nb))
+
+
+def check_scores_chunks_and_permutation(O):
+    """Row chunks (rowStart, numRows) are slices of the full matrix; permuting the 128 dims of
+    q and kbar together changes no logit (each head dot is exact before its one rounding)."""
+    rng = np.random.default_rng(71)
+    for dt in ("bf16", "f16"):
+        B, S = 2, 64
+        nb = S // 4
+        from sparse_attention_indexer_qsa_amd.workloads import to_bits
+        q = to_bits(rng.standard_normal((B, S, 4, 128), dtype=np.float32), dt)
+        kb = to_bits(rng.standard_normal((B, nb, 128), dtype=np.float32), dt)
+        ctx = np.array([64, 50], np.int32)
+        full = O.scores(q, kb, ctx, 0, B * S, dt)
+        parts = [O.scores(q, kb, ctx, r0, n, dt) for r0, n in ((0, 37), (37, 60), (97, 31))]
+        assert np.array_equal(np.concatenate(parts).view(np.uint32), full.view(np.uint32))
+        perm = rng.permutation(128)
+        qp = np.ascontiguousarray(q[..., perm])
+        kp = np.ascontiguousarray(kb[..., perm])
+        assert np.array_equal(O.scores(qp, kp, ctx, 0, B * S, dt).view(np.uint32),
+                              full.view(np.uint32))
+
+
+def check_scores_numpy(O):
+    """An independent numpy derivation (float64 matmul of the widened values, one rounding to
+    float32 per head, ReLU, ascending head sum, scale) matches bit for bit."""
+    rng = np.random.default_rng(73)
+    dt = "bf16"
+    B, S = 2, 48
+    nb = S // 4
+    q = _bf16(rng.standard_normal((B, S, 4, 128)))
+    kb = _bf16(rng.standard_normal((B, nb, 128)))
+    ctx = np.array([48, 30], np.int32)
+    got = O.scores(q, kb, ctx, 0, B * S, dt).reshape(B, S, nb)
+    qf, kf = nm.widen(q, dt).astype(np.float64), nm.widen(kb, dt).astype(np.float64)
+    dots = np.einsum("bthd,bgd->bthg", qf, kf).astype(np.float32)
+    r = np.maximum(dots, np.float32(0))
+    ssum = ((r[:, :, 0] + r[:, :, 1]) + r[:, :, 2]) + r[:, :, 3]
+    ref = np.float32(1) / np.sqrt(np.float32(128)) * ssum
+    t = np.arange(S)[:, None]
+    g = np.arange(nb)[None, :]
+    vis = (g < (t + 1) // 4)[None] & (t < ctx[:, None, None])
+    ref = np.where(vis, ref, np.float32(-np.finfo(np.float32).max))
+    assert np.array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+def check_scores_decode_matches_prefill(O):
+    """launchQsaIndexScoresDecode: the decode token t = ctx-1 scored against kbar gathered from
+    the V-tails equals row t of the prefill scores over [0, ctx/4); entries past the prefix are
+    not written; blocks whose V page is unused score -FLT_MAX."""
+    from oracle.ref import Pool
+    rng = np.random.default_rng(79)
+    dt = "bf16"
+    L = np.array([300, 131, 8, 3], np.int32)
+    x, wQ, wK, cs, pt, numPages = _history(rng, dt, L)
+    B, Lmax = x.shape[:2]
+    nb = (Lmax + 3) // 4
+    data = np.full((2 * numPages, 128, 2, 384), 0xA5A5, np.uint16)
+    pool = Pool(data, pt, numPages, 256)
+    kb = O.k_compress(x, cs, L, wK, 1e-6, nb, 0, nb, 0, dt, pool=pool)
+    q = O.q_prep(x, cs, L, wQ, 1e-6, dt)
+    full = O.scores(q, kb, L, 0, B * Lmax, dt).reshape(B, Lmax, nb)
+    qdec = np.stack([q[b, L[b] - 1] for b in range(B)])
+    lg = O.scores_decode(qdec, L, pool, nb, dt)
+    for b in range(B):
+        n = L[b] // 4
+        assert np.array_equal(lg[b, :n].view(np.uint32), full[b, L[b] - 1, :n].view(np.uint32))
+        assert np.all(np.isnan(lg[b, n:]))
+    pt2 = pt.copy()
+    pt2[0, 1, 1] = -1                       # blocks 32..63 of sequence 0 lose their V page
+    lg2 = O.scores_decode(qdec, L, Pool(data, pt2, numPages, 256), nb, dt)
+    assert np.all(lg2[0, 32:64].view(np.uint32) == NEG_FLT_MAX_BITS)
+    assert np.array_equal(lg2[0, :32], lg[0, :32]) and np.array_equal(lg2[0, 64:75], lg[0, 64:75])
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -47,6 +47,14 @@ MUTANTS = {
                                          "int64_t t0 = p;\n    for"),
     "decode_past_keys_wrong_plane": ("int64_t off = pool_tail_offset(pool, b, 0, t);\n          if (off < 0) ok = 0;",
                                      "int64_t off = pool_tail_offset(pool, b, 1, t);\n          if (off < 0) ok = 0;"),
+    "score_relu_after_sum": ("float relu = dot > 0.0f ? dot : 0.0f;\n    sum = sum + relu;\n  }\n  return score_scale() * sum;",
+                             "sum = sum + dot;\n  }\n  return score_scale() * (sum > 0.0f ? sum : 0.0f);"),
+    "score_scale_before_sum": ("sum = sum + relu;\n  }\n  return score_scale() * sum;",
+                               "sum = sum + score_scale() * relu;\n  }\n  return sum;"),
+    "score_nvis_off_by_one": ("int64_t nVis = (t + 1) / 4;", "int64_t nVis = (t + 4) / 4;"),
+    "score_padding_rule": ("if (c <= 0 || t >= c) {", "if (c <= 0 || t > c) {"),
+    "score_decode_plane": ("int64_t off = pool_tail_offset(pool, b, 1, 4 * g);\n      logits",
+                           "int64_t off = pool_tail_offset(pool, b, 0, 4 * g);\n      logits"),
     "rsqrt_single": ("float inv = (float)(1.0 / sqrt((double)v));",
                      "float inv = 1.0f / (float)sqrt((double)v) * (1.0f + 1.2e-7f);"),
 }
