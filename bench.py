@@ -27,12 +27,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "indexer rows/s and achieved HBM GB/s (% of peak), bf16, QPrep+KCompress+persist"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "sparse_attention_indexer_qsa_amd", "csrc", "qsa_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sparse_attention_indexer_qsa_amd", "csrc", f)
+               for f in ("qsa_kernels.hip", "qsa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_kernel_long_prefill.json")
 
 
 def kernel_source_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the sources of the fused prefill kernel (its kernel file and device helpers)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(wl):
@@ -132,6 +137,39 @@ def decode_leg(qsa, torch, steps, warmup):
             "blocks_compressed_per_call": blocks}
 
 
+def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=65536, numRows=8192):
+    """Block scores (qsa_index_scores, MFMA) over a chunk of the long prefill's query rows,
+    on the qNormed and kbar the fused prefill produced.  Bound by the FP32 logits it writes."""
+    import numpy as np
+    S, nb = wl.S, wl.numBlocks
+    logits = torch.empty(numRows, nb, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    args = (logits.data_ptr(), s["q"].data_ptr(), s["kb"].data_ptr(), s["ctx"].data_ptr(), 1, S,
+            nb, rowStart, numRows, qsa.QSA_BF16, stream.cuda_stream)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            assert qsa.lib.qsa_index_scores(*args) == 0, qsa.qsa_last_error()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            qsa.lib.qsa_index_scores(*args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    t = rowStart + np.arange(numRows)
+    visible = int(np.minimum((t + 1) // 4, nb).sum())
+    nvis_max = int(min((rowStart + numRows) // 4, nb))
+    alg = 4 * numRows * nb + 1024 * numRows + 256 * nvis_max
+    flops = 2 * 4 * 128 * visible
+    del logits
+    return {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks, "
+                        f"bf16, FP32 logits", "entry": "qsa_index_scores", "us_per_call": us,
+            "alg_bytes": alg, "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS,
+            "visible_scores": visible, "TFLOPs": flops / us / 1e6,
+            "mfma_bf16_frac": flops / us / 1e6 / 2500.0}
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -158,9 +196,9 @@ PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/ptrace -o run -- "
              "python3 $R/bench.py --steps 50 --warmup 10 --no-cpu",
     "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pfetch -o run "
-             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --no-scores --copy-calib",
     "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pwrite -o run "
-             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --no-scores --copy-calib",
 }
 
 
@@ -192,7 +230,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     pre = [r for r in stats if "prefill_kernel" in r["Name"]][0]
     avg_us = float(pre["AverageNs"]) / 1e3
     md = [f"# prefill_kernel (fused K1a + K1b + persist) — long prefill, B=1, S=131072, bf16", "",
-          f"Kernel source hash (first 16 hex of sha256 of `qsa_kernels.hip`): "
+          f"Kernel source hash (first 16 hex of sha256 of `qsa_kernels.hip` + `qsa_device.h`): "
           f"`{kernel_source_hash()}`.  MI355X (gfx950), one GPU.",
           f"Algorithmic bytes per launch: {alg:,}.", "", "## Kernel durations", "",
           "Command (run from `/tmp` with `TMPDIR=/tmp`; `R` is the repository root):", "",
@@ -232,6 +270,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-three-call", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode pre-pass leg")
+    ap.add_argument("--no-scores", action="store_true", help="skip the block-scores leg")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -346,6 +385,10 @@ def main():
             torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
 
+    scores = None
+    if not args.no_scores:
+        print("[bench] timing the block scores", file=sys.stderr, flush=True)
+        scores = scores_leg(qsa, torch, sets[0], wl, min(args.steps, 50), min(args.warmup, 5))
     decode = None
     if not args.no_decode:
         print("[bench] timing the decode pre-pass", file=sys.stderr, flush=True)
@@ -378,6 +421,7 @@ def main():
                    "source_sha256_16": kernel_source_hash()},
         "three_call": three,
         "decode_pre_pass": decode,
+        "scores": scores,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

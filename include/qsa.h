@@ -217,6 +217,36 @@ int qsa_index_pre_decode(void* qNormed, const void* indexQk, const float* cosSin
                          qsa_dtype dt, void* stream);
 
 /*
+ * Block-relevance scores, prefill ("Qsa Indexer Kernels": launchQsaIndexScores).
+ *
+ * logits   [out] FP32 [numRows, numBlocks]: row i is global row r = rowStart + i = b*S + t.
+ * qNormed  [in]  T [B, S, 4, 128] (qsa_index_q_prep);  kbar [in] T [B, numBlocks, 128].
+ * contextLengths [in] device int32 [B].   0 <= rowStart, rowStart + numRows <= B*S.
+ * logits[i][g] = (1/sqrtf(128)) * sum_{h<4, ascending} relu(q[r][h] . kbar[b][g]), FP32 dots,
+ * ReLU per head, the scale after the sum; g >= (t+1)/4 (not a complete block up to t) gives
+ * -FLT_MAX; a padded row (t >= ctx[b], or ctx[b] <= 0) is -FLT_MAX throughout and its q row is
+ * not read.  The dot products run on MFMA; their summation order is the hardware's.
+ * numBlocks <= 65535*2048.
+ */
+int qsa_index_scores(float* logits, const void* qNormed, const void* kbar,
+                     const int32_t* contextLengths, int32_t batchSize, int32_t seqLen,
+                     int32_t numBlocks, int32_t rowStart, int32_t numRows, qsa_dtype dt,
+                     void* stream);
+
+/*
+ * Block-relevance scores, decode ("Qsa Indexer Kernels": launchQsaIndexScoresDecode).
+ *
+ * logits   [out] FP32 [B, maxBlocks]; only [0, min(ctx/4, maxBlocks)) of each row is written.
+ * qNormed  [in]  T [B, 1, 4, 128] (one query token per sequence).
+ * contextLengths [in] device int32 [B]: TOTAL lengths.   pool: required (kbar is read from the
+ * V-tail of token 4g).  Same score as qsa_index_scores; a block whose V page entry is unused
+ * or out of range scores -FLT_MAX.  maxBlocks <= 65535*64.
+ */
+int qsa_index_scores_decode(float* logits, const void* qNormed, const int32_t* contextLengths,
+                            const qsa_pool_state_t* pool, int32_t batchSize, int32_t maxBlocks,
+                            qsa_dtype dt, void* stream);
+
+/*
  * Debug forms: the same kernels with their FP32 intermediates written out.  Arguments as the
  * entry point of the same name, plus (all device FP32 unless noted, all required):
  *   qsa_debug_q_prep:     meanSq [B,S,4], invRms [B,S,4], preCast [B,S,4,128];

@@ -34,16 +34,20 @@ def _run(cmd):
 
 
 def build(hipcc="hipcc"):
-    """Compile and link libqsa.so (always recompiles)."""
+    """Compile and link libqsa.so (always recompiles): every .hip kernel source of csrc/ and
+    the C ABI layer."""
+    import glob
     os.makedirs(BUILD, exist_ok=True)
-    kobj = os.path.join(BUILD, "qsa_kernels.o")
+    objs = []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+        _run([hipcc, *COMMON, *DEVICE, "-c", src, "-o", obj])
+        objs.append(obj)
     aobj = os.path.join(BUILD, "qsa_api.o")
-    _run([hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "qsa_kernels.hip"), "-o", kobj])
     _run([hipcc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I",
-          os.path.join(ROCM, "include"), "-c",
-          os.path.join(CSRC, "qsa_api.cpp"), "-o", aobj])
+          os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, "qsa_api.cpp"), "-o", aobj])
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", kobj, aobj, "-o", tmp])
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, aobj, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

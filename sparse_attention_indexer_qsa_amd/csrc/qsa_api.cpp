@@ -321,6 +321,68 @@ QSA_EXPORT int qsa_index_pre_decode(void* qNormed, const void* indexQk, const fl
                   "qsa_index_pre_decode");
 }
 
+QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* kbar,
+                                const int32_t* contextLengths, int32_t batchSize, int32_t seqLen,
+                                int32_t numBlocks, int32_t rowStart, int32_t numRows, qsa_dtype dt,
+                                void* stream) {
+  qsa::Dt t;
+  TRY(check_dt(dt, &t));
+  if (batchSize < 0 || seqLen < 0 || numBlocks < 0 || rowStart < 0 || numRows < 0)
+    return fail(QSA_E_INVALID, "batchSize = %d, seqLen = %d, numBlocks = %d, rowStart = %d, "
+                "numRows = %d must be >= 0", batchSize, seqLen, numBlocks, rowStart, numRows);
+  const int64_t rows = (int64_t)batchSize * seqLen;
+  if ((int64_t)rowStart + numRows > rows)
+    return fail(QSA_E_INVALID, "rowStart + numRows = %lld > batchSize * seqLen = %lld",
+                (long long)rowStart + numRows, (long long)rows);
+  if (numRows == 0 || numBlocks == 0) return ok();
+  if ((numBlocks + 2047) / 2048 > 65535)
+    return fail(QSA_E_INVALID, "numBlocks = %d exceeds the supported %d", numBlocks,
+                65535 * 2048);
+  TRY(need(logits, "logits", 4));
+  TRY(need(qNormed, "qNormed", 16));
+  TRY(need(kbar, "kbar", 16));
+  TRY(need(contextLengths, "contextLengths", 4));
+  qsa::ScoresArgs a{};
+  a.logits = logits;
+  a.qNormed = qNormed;
+  a.kbar = kbar;
+  a.ctx = contextLengths;
+  a.B = batchSize;
+  a.S = seqLen;
+  a.numBlocks = numBlocks;
+  a.rowStart = rowStart;
+  a.numRows = numRows;
+  a.tilesPerSeq = ceil_div(seqLen, 32);
+  const int64_t last = (int64_t)rowStart + numRows - 1;
+  a.tile0 = (rowStart / seqLen) * a.tilesPerSeq + (rowStart % seqLen) / 32;
+  a.numTiles = (last / seqLen) * a.tilesPerSeq + (last % seqLen) / 32 - a.tile0 + 1;
+  TRY(check_grid(a.numTiles));
+  (void)hipGetLastError();
+  return launched(qsa::launch_scores(a, t, static_cast<hipStream_t>(stream)), "qsa_index_scores");
+}
+
+QSA_EXPORT int qsa_index_scores_decode(float* logits, const void* qNormed,
+                                       const int32_t* contextLengths,
+                                       const qsa_pool_state_t* pool, int32_t batchSize,
+                                       int32_t maxBlocks, qsa_dtype dt, void* stream) {
+  qsa::Dt t;
+  TRY(check_dt(dt, &t));
+  if (batchSize < 0 || maxBlocks < 0)
+    return fail(QSA_E_INVALID, "batchSize = %d, maxBlocks = %d", batchSize, maxBlocks);
+  if (batchSize == 0 || maxBlocks == 0) return ok();
+  if ((maxBlocks + 63) / 64 > 65535)
+    return fail(QSA_E_INVALID, "maxBlocks = %d exceeds the supported %d", maxBlocks, 65535 * 64);
+  TRY(need(logits, "logits", 4));
+  TRY(need(qNormed, "qNormed", 16));
+  TRY(need(contextLengths, "contextLengths", 4));
+  qsa::PoolArgs p{};
+  TRY(check_pool(pool, &p));
+  const qsa::ScoresDecodeArgs a{logits, qNormed, contextLengths, p, batchSize, maxBlocks};
+  (void)hipGetLastError();
+  return launched(qsa::launch_scores_decode(a, t, static_cast<hipStream_t>(stream)),
+                  "qsa_index_scores_decode");
+}
+
 QSA_EXPORT const char* qsa_last_error(void) { return g_err; }
 
 QSA_EXPORT int qsa_abi_version(void) { return QSA_ABI_VERSION; }

@@ -94,11 +94,33 @@ struct PreDecodeArgs {
   PoolArgs pool;
 };
 
+// Block scores over global rows [rowStart, rowStart + numRows); workgroup tiles of 32 tokens
+// of one sequence, numTiles of them starting at tile0 (tile = b * tilesPerSeq + t / 32).
+struct ScoresArgs {
+  float* logits;
+  const void* qNormed;
+  const void* kbar;
+  const int32_t* ctx;
+  int32_t B, S, numBlocks;
+  int64_t rowStart, numRows;
+  int64_t tile0, tilesPerSeq, numTiles;
+};
+
+struct ScoresDecodeArgs {
+  float* logits;
+  const void* qNormed;
+  const int32_t* ctx;
+  PoolArgs pool;
+  int32_t B, maxBlocks;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.  Arguments are already validated.
 hipError_t launch_q_prep(const QPrepArgs& a, Dt dt, bool debug, hipStream_t stream);
 hipError_t launch_k_compress(const KCompressArgs& a, Dt dt, bool debug, hipStream_t stream);
 hipError_t launch_persist(const PersistArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_pre_decode(const PreDecodeArgs& a, Dt dt, hipStream_t stream);
+hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream);
+hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream);
 
 }  // namespace qsa

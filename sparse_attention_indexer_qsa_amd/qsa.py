@@ -50,6 +50,8 @@ def _declare(lib):
         "qsa_index_persist": [P, P, P, P, I, I, I, I, I, I, P, ctypes.c_int, P],
         "qsa_index_prefill": [P, P, P, P, I, P, P, P, F, P, I, I, I, ctypes.c_int, P],
         "qsa_index_pre_decode": [P, P, P, I, P, P, P, P, F, P, I, I, ctypes.c_int, P],
+        "qsa_index_scores": [P, P, P, P, I, I, I, I, I, ctypes.c_int, P],
+        "qsa_index_scores_decode": [P, P, P, P, I, I, ctypes.c_int, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -257,6 +259,35 @@ def qsa_index_pre_decode(qNormed, indexQk, cosSin, contextLengths, wQ, wK, rmsEp
                                     _dev(wQ, "wQ", HEAD_DIM, _T), _dev(wK, "wK", HEAD_DIM, _T),
                                     float(rmsEps), ctypes.byref(pool.c_struct(B)), B, S,
                                     _dt_of(indexQk, dt), _stream(stream)))
+
+
+def qsa_index_scores(logits, qNormed, kbar, contextLengths, numBlocks, rowStart, numRows,
+                     batchSize=None, seqLen=None, dt=None, stream=None):
+    """Block scores of global rows [rowStart, rowStart+numRows): logits FP32 [numRows,
+    numBlocks] from qNormed [B,S,4,128] and kbar [B,numBlocks,128]."""
+    B = qNormed.shape[0] if batchSize is None else batchSize
+    S = qNormed.shape[1] if seqLen is None else seqLen
+    if numRows == 0 or numBlocks == 0:
+        return
+    _check(lib.qsa_index_scores(_dev(logits, "logits", numRows * numBlocks, _F32),
+                                _dev(qNormed, "qNormed", B * S * HEADS * HEAD_DIM, _T),
+                                _dev(kbar, "kbar", B * numBlocks * HEAD_DIM, _T),
+                                _dev(contextLengths, "contextLengths", B, _I32), B, S, numBlocks,
+                                rowStart, numRows, _dt_of(qNormed, dt), _stream(stream)))
+
+
+def qsa_index_scores_decode(logits, qNormed, contextLengths, pool, maxBlocks, batchSize=None,
+                            dt=None, stream=None):
+    """Decode block scores against the V-tails: logits FP32 [B, maxBlocks], prefix
+    [0, ctx/4) of each row written."""
+    B = qNormed.shape[0] if batchSize is None else batchSize
+    if B == 0 or maxBlocks == 0:
+        return
+    _check(lib.qsa_index_scores_decode(_dev(logits, "logits", B * maxBlocks, _F32),
+                                       _dev(qNormed, "qNormed", B * HEADS * HEAD_DIM, _T),
+                                       _dev(contextLengths, "contextLengths", B, _I32),
+                                       ctypes.byref(pool.c_struct(B)), B, maxBlocks,
+                                       _dt_of(qNormed, dt), _stream(stream)))
 
 
 def qsa_last_error():

@@ -1,0 +1,163 @@
+"""GPU parity of the block scores (qsa_index_scores on MFMA, qsa_index_scores_decode) through
+the C ABI.  Masked and padded entries must be exactly -FLT_MAX; scores are compared within the
+FP32 summation bound: |gpu - ref| <= c * 2^-16 * sum_h sum_d |q_hd k_d| + 2^-22 |ref|, where c =
+1/sqrtf(128) (128-term dots in FP32: n*u = 2^-17 relative to the sum of |products|, doubled;
+then three head additions and the scale)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_indexer_qsa_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+NEG = np.float32(-np.finfo(np.float32).max)
+
+
+@pytest.fixture(scope="module")
+def qsa():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import sparse_attention_indexer_qsa_amd.qsa as q
+    return q
+
+
+@pytest.fixture(scope="module")
+def O():
+    from oracle.ref import default
+    return default()
+
+
+def _abs_bound(q, kb, dt, rows, ctx, S):
+    """c * sum_h sum_d |q_hd k_d| for global `rows` against every block of its sequence, as
+    (sum_h |q_h|) . |k| per sequence."""
+    qsum = np.abs(G.widen(q.reshape(-1, 4, 128)[rows], dt)).sum(axis=1)   # [R, 128]
+    kf = np.abs(G.widen(kb, dt))                                          # [B, nb, 128]
+    b = rows // S
+    out = np.empty((len(rows), kb.shape[1]))
+    for bb in np.unique(b):
+        sel = b == bb
+        out[sel] = qsum[sel] @ kf[bb].T
+    return (1 / np.sqrt(128.0)) * out
+
+
+def check_logits(got, ref, bound, what):
+    gbits, rbits = got.view(np.uint32), ref.view(np.uint32)
+    neg = ref == NEG
+    assert np.array_equal(gbits[neg], rbits[neg]), f"{what}: -FLT_MAX entries differ"
+    assert np.all(got[~neg] != NEG), f"{what}: visible entry masked"
+    err = np.abs(got[~neg].astype(np.float64) - ref[~neg].astype(np.float64))
+    tol = 2.0 ** -16 * bound[~neg] + 2.0 ** -22 * np.abs(ref[~neg].astype(np.float64)) + 1e-30
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} beyond tolerance, max err/tol " \
+        f"{float((err / tol).max()):.3g}"
+    return int((gbits != rbits).sum()), float((err / tol).max()) if err.size else 0.0
+
+
+def _inputs(O, wl):
+    q = O.q_prep(wl.indexQk, wl.cosSin, wl.ctx, wl.wQ, wl.eps, wl.dt)
+    kb = O.k_compress(wl.indexQk, wl.cosSin, wl.ctx, wl.wK, wl.eps, wl.numBlocks, 0,
+                      wl.numBlocks, 0, wl.dt)
+    return q, kb
+
+
+def _gpu_scores(qsa, q, kb, ctx, dt, rowStart, numRows, nb):
+    out = G.Guarded((numRows, nb), torch.float32, fill=float("nan"))
+    qsa.qsa_index_scores(out.t, G.dev_bits(q), G.dev_bits(kb), G.dev(ctx), nb, rowStart,
+                         numRows, dt=dt)
+    torch.cuda.synchronize()
+    out.check()
+    return out.t.cpu().numpy()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_scores_batched_prefill_full(qsa, O, dt):
+    """All 16384 rows x 512 blocks of the batched prefill (lengths 0, 2048, ragged, NaN
+    padding), K1a/K1b outputs of the oracle as inputs."""
+    wl = W.config2(dt)
+    q, kb = _inputs(O, wl)
+    rows = wl.B * wl.S
+    got = _gpu_scores(qsa, q, kb, wl.ctx, dt, 0, rows, wl.numBlocks)
+    ref = O.scores(q, kb, wl.ctx, 0, rows, dt)
+    bound = _abs_bound(q, kb, dt, np.arange(rows), wl.ctx, wl.S)
+    nd, worst = check_logits(got, ref, bound, f"batched {dt}")
+    print(f"[parity] scores batched {dt}: {nd} of {got.size} differ in bits, worst err/tol "
+          f"{worst:.3g}", flush=True)
+
+
+def test_scores_long_prefill_chunk(qsa, O):
+    """The long prefill (S=131072, 32768 blocks): a 2048-row chunk from the middle, sampled
+    rows checked one by one against the oracle; every row's mask checked."""
+    wl = W.config3()
+    q, kb = _inputs(O, wl)
+    r0, n = 65536 + 13, 2048
+    got = _gpu_scores(qsa, q, kb, wl.ctx, wl.dt, r0, n, wl.numBlocks)
+    t = r0 + np.arange(n)
+    nvis = (t + 1) // 4
+    g = np.arange(wl.numBlocks)
+    assert np.all((got == NEG) == (g[None, :] >= nvis[:, None]))
+    rng = np.random.default_rng(3)
+    sample = np.sort(rng.choice(n, 24, replace=False))
+    for i in sample:
+        ref = O.scores(q, kb, wl.ctx, r0 + int(i), 1, wl.dt)
+        bound = _abs_bound(q, kb, wl.dt, np.array([r0 + int(i)]), wl.ctx, wl.S)
+        check_logits(got[i:i + 1], ref, bound, f"long row {r0 + i}")
+
+
+def test_scores_chunks_and_edges(qsa, O):
+    """Ragged S (not a multiple of the 32-token tile), chunks that start mid-tile and span
+    sequences, a length-0 sequence: chunks equal slices of one GPU call bit for bit, and match
+    the oracle."""
+    rng = np.random.default_rng(97)
+    dt = "bf16"
+    B, S = 3, 203
+    nb = (S + 3) // 4
+    q = W.to_bits(rng.standard_normal((B, S, 4, 128), dtype=np.float32), dt)
+    kb = W.to_bits(rng.standard_normal((B, nb, 128), dtype=np.float32), dt)
+    ctx = np.array([203, 0, 150], np.int32)
+    q[2, 150:] = 0x7FC0                      # padded rows are never read
+    full = _gpu_scores(qsa, q, kb, ctx, dt, 0, B * S, nb)
+    ref = O.scores(q, kb, ctx, 0, B * S, dt)
+    check_logits(full, ref, _abs_bound(q, kb, dt, np.arange(B * S), ctx, S), "edges")
+    for r0, n in ((0, 1), (5, 37), (190, 40), (201, 250), (600, 9)):
+        part = _gpu_scores(qsa, q, kb, ctx, dt, r0, n, nb)
+        assert np.array_equal(part.view(np.uint32), full[r0:r0 + n].view(np.uint32)), (r0, n)
+
+
+def test_scores_decode(qsa, O):
+    """Decode scores of one query token per sequence against V-tails written by a GPU prefill
+    (K1b with the pool); entries past each row's prefix keep their content; unused V pages
+    score -FLT_MAX."""
+    rng = np.random.default_rng(101)
+    dt = "bf16"
+    L = np.array([4000, 1031, 7, 3, 2048, 513, 0, 64], np.int32)
+    B, Lmax = len(L), int(L.max())
+    x = W.to_bits(rng.standard_normal((B, Lmax, 640), dtype=np.float32), dt)
+    wK = W.to_bits(0.1 * rng.standard_normal(128, dtype=np.float32), dt)
+    m = (Lmax + 127) // 128
+    numPages = B * m
+    pt = np.stack([rng.permutation(numPages)[:B * m].reshape(B, m),
+                   rng.permutation(numPages)[:B * m].reshape(B, m) + numPages], 1).astype(np.int32)
+    pt[1, 1, 3] = -1
+    spec = W.PoolSpec(numPages, pt)
+    cs = W.cos_sin_table(Lmax + 8, 1e4)
+    nb = (Lmax + 3) // 4
+    pool = G.device_pool(spec)
+    kbd = torch.empty(B, nb, 128, dtype=torch.int16, device="cuda")
+    qsa.qsa_index_k_compress(kbd, G.dev_bits(x), G.dev(cs), G.dev(L), G.dev_bits(wK), 1e-6, nb,
+                             0, nb, 0, pool=pool, dt=dt)
+    qdec = W.to_bits(rng.standard_normal((B, 1, 4, 128), dtype=np.float32), dt)
+    out = torch.full((B, nb), float("nan"), device="cuda")
+    qsa.qsa_index_scores_decode(out, G.dev_bits(qdec), G.dev(L), pool, nb, dt=dt)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    from oracle.ref import Pool
+    rpool = Pool(G.host_bits(pool.pool).copy(), pt, numPages, 256)
+    ref = O.scores_decode(qdec, L, rpool, nb, dt)
+    for b in range(B):
+        n = int(L[b]) // 4
+        assert np.all(np.isnan(got[b, n:]))
+        kbh = G.host_bits(kbd)
+        bound = (1 / np.sqrt(128.0)) * np.einsum(
+            "hd,gd->g", np.abs(G.widen(qdec[b, 0], dt)), np.abs(G.widen(kbh[b, :n], dt)))
+        check_logits(got[b, :n], ref[b, :n], bound, f"decode seq {b}")
+    assert np.all(got[1, 96:128] == NEG)
