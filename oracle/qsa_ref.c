@@ -30,6 +30,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -493,6 +494,150 @@ void ref_scores_decode(float* logits, const uint16_t* qNormed, const int32_t* ct
 }
 
 float ref_score_scale(void) { return score_scale(); }
+
+/* --------------------------------------------------------------- selection + expand ---- */
+
+enum { TOPK = 512, INDEX_WIDTH = 2051 };
+
+/* launchQsaIndexIdsFill: ids[r * numBlocks + c] = c. */
+void ref_ids_fill(int32_t* ids, int32_t numRows, int32_t numBlocks) {
+  for (int64_t r = 0; r < numRows; ++r)
+    for (int64_t c = 0; c < numBlocks; ++c) ids[r * numBlocks + c] = (int32_t)c;
+}
+
+/*
+ * The monotone map of binary32 bit patterns to unsigned integers used for the selection
+ * ("Qsa Indexer Kernels", launchQsaTopKExpandDecode): u = bits >= 0 ? bits | 0x80000000 : ~bits
+ * (bits read as a signed integer).  Larger floats map to larger u; -0 maps just below +0.
+ */
+static uint32_t orderable(float f) {
+  uint32_t b = f32_bits(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+/*
+ * launchQsaIndexExpand for one row (also the expand step e. of launchQsaTopKExpandDecode):
+ * out[4i+j] = sel[i]*4 + j for i < kSel, then the tail tokens out[4*kSel + j] = 4*nVis + j for
+ * j < tail (always appended), then -1 up to 2051 slots.  `sel` is read only for i < kSel.
+ */
+static void expand_row(int32_t* out, const int32_t* sel, int64_t kSel, int64_t nVis,
+                       int64_t tail) {
+  int64_t n = 0;
+  for (int64_t i = 0; i < kSel; ++i)
+    for (int j = 0; j < 4; ++j) out[n++] = sel[i] * 4 + j;
+  for (int64_t j = 0; j < tail; ++j) out[n++] = (int32_t)(4 * nVis + j);
+  while (n < INDEX_WIDTH) out[n++] = -1;
+}
+
+static int64_t k_sel(int64_t nVis) { return nVis < TOPK ? nVis : TOPK; }
+
+/*
+ * launchQsaIndexExpand: rows r = b*S + t in [rowStart, rowStart + numRows) of outIdx
+ * [B*S, 2051]; a padded row (t >= ctx[b], or ctx[b] <= 0) is all -1 and reads nothing.
+ */
+void ref_expand(int32_t* outIdx, const int32_t* sortedIds, const int32_t* ctx, int32_t B,
+                int32_t S, int32_t numBlocks, int32_t rowStart, int32_t numRows) {
+  (void)B;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < numRows; ++i) {
+    int64_t r = rowStart + i, b = r / S, t = r % S;
+    int32_t* out = outIdx + r * INDEX_WIDTH;
+    if (ctx[b] <= 0 || t >= ctx[b]) {
+      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;
+      continue;
+    }
+    int64_t nVis = (t + 1) / 4;
+    expand_row(out, sortedIds + i * numBlocks, k_sel(nVis), nVis, (t + 1) % 4);
+  }
+}
+
+/* Descending by orderable key; equal keys in ascending id (a stable sort over ascending ids). */
+typedef struct { uint32_t key; int32_t id; } keyed_t;
+static int by_key_desc_id_asc(const void* x, const void* y) {
+  const keyed_t *a = (const keyed_t*)x, *b = (const keyed_t*)y;
+  if (a->key != b->key) return a->key > b->key ? -1 : 1;
+  return a->id < b->id ? -1 : (a->id > b->id);
+}
+
+/*
+ * The prefill selection of the page's pipeline: ids filled per row (launchQsaIndexIdsFill),
+ * sorted by descending logit with a stable radix sort over ascending ids (equal logits keep
+ * ascending id order), then launchQsaIndexExpand.  Written here as exactly that: a full sort of
+ * each row's numBlocks (key, id) pairs, then expand_row.  Also returns the sorted ids.
+ */
+void ref_topk_expand(int32_t* outIdx, int32_t* sortedIds /*nullable*/, const float* logits,
+                     const int32_t* ctx, int32_t B, int32_t S, int32_t numBlocks,
+                     int32_t rowStart, int32_t numRows) {
+  (void)B;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t i = 0; i < numRows; ++i) {
+    int64_t r = rowStart + i, b = r / S, t = r % S;
+    int32_t* out = outIdx + r * INDEX_WIDTH;
+    keyed_t* kv = (keyed_t*)malloc(sizeof(keyed_t) * (numBlocks > 0 ? numBlocks : 1));
+    int32_t* sorted = (int32_t*)malloc(sizeof(int32_t) * (numBlocks > 0 ? numBlocks : 1));
+    for (int64_t g = 0; g < numBlocks; ++g) {
+      kv[g].key = orderable(logits[i * numBlocks + g]);
+      kv[g].id = (int32_t)g;
+    }
+    qsort(kv, (size_t)numBlocks, sizeof(keyed_t), by_key_desc_id_asc);
+    for (int64_t g = 0; g < numBlocks; ++g) sorted[g] = kv[g].id;
+    if (sortedIds) memcpy(sortedIds + i * numBlocks, sorted, sizeof(int32_t) * numBlocks);
+    if (ctx[b] <= 0 || t >= ctx[b]) {
+      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;
+    } else {
+      int64_t nVis = (t + 1) / 4;
+      expand_row(out, sorted, k_sel(nVis < numBlocks ? nVis : numBlocks), nVis, (t + 1) % 4);
+    }
+    free(kv);
+    free(sorted);
+  }
+}
+
+/*
+ * launchQsaTopKExpandDecode (without the split counters, which belong to the attention
+ * kernel): per sequence, nVis = ctx/4 (capped at maxBlocks), kSel = min(512, nVis),
+ * tail = ctx%4.  nVis <= 512 selects every block.  Otherwise the selected set is the kSel
+ * largest orderable keys of logits[b][0, nVis), equal keys at the threshold taken in ascending
+ * block id; the selection is emitted in ascending block id order (a fixed-order scan), expanded
+ * to 4 tokens each, followed by the tail tokens [4*nVis, ctx) and -1 padding to 2051.
+ * ctx <= 0 gives an all -1 row.
+ */
+void ref_topk_expand_decode(int32_t* outIdx, const float* logits, const int32_t* ctx, int32_t B,
+                            int32_t maxBlocks) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < B; ++b) {
+    int32_t* out = outIdx + b * INDEX_WIDTH;
+    int64_t c = ctx[b];
+    if (c <= 0) {
+      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;
+      continue;
+    }
+    int64_t nVis = c / 4;
+    if (nVis > maxBlocks) nVis = maxBlocks;
+    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (nVis > 0 ? nVis : 1));
+    int64_t kSel = k_sel(nVis);
+    if (nVis <= TOPK) {
+      for (int64_t g = 0; g < nVis; ++g) sel[g] = (int32_t)g;
+    } else {
+      keyed_t* kv = (keyed_t*)malloc(sizeof(keyed_t) * nVis);
+      for (int64_t g = 0; g < nVis; ++g) {
+        kv[g].key = orderable(logits[b * maxBlocks + g]);
+        kv[g].id = (int32_t)g;
+      }
+      qsort(kv, (size_t)nVis, sizeof(keyed_t), by_key_desc_id_asc);
+      /* the first kSel of this order are the selected set; emit them by ascending id */
+      char* pick = (char*)calloc((size_t)nVis, 1);
+      for (int64_t i = 0; i < kSel; ++i) pick[kv[i].id] = 1;
+      int64_t n = 0;
+      for (int64_t g = 0; g < nVis; ++g)
+        if (pick[g]) sel[n++] = (int32_t)g;
+      free(pick);
+      free(kv);
+    }
+    expand_row(out, sel, kSel, nVis, c % 4);
+    free(sel);
+  }
+}
 
 /* ------------------------------------------------------------------------- utilities ---- */
 

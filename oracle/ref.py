@@ -90,12 +90,17 @@ class Oracle:
         L.ref_scores.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_int]
         L.ref_scores_decode.argtypes = [P, P, P, P, I32, I32, ctypes.c_int]
         L.ref_score_scale.restype = ctypes.c_float
+        L.ref_ids_fill.argtypes = [P, I32, I32]
+        L.ref_expand.argtypes = [P, P, P, I32, I32, I32, I32, I32]
+        L.ref_topk_expand.argtypes = [P, P, P, P, I32, I32, I32, I32, I32]
+        L.ref_topk_expand_decode.argtypes = [P, P, P, I32, I32]
         L.ref_widen.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_narrow.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_set_threads.argtypes = [ctypes.c_int]
         L.ref_max_threads.restype = ctypes.c_int
         for f in (L.ref_q_prep, L.ref_k_compress, L.ref_persist, L.ref_widen, L.ref_narrow,
-                  L.ref_set_threads, L.ref_pre_decode, L.ref_scores, L.ref_scores_decode):
+                  L.ref_set_threads, L.ref_pre_decode, L.ref_scores, L.ref_scores_decode,
+                  L.ref_ids_fill, L.ref_expand, L.ref_topk_expand, L.ref_topk_expand_decode):
             f.restype = None
         self.L = L
 
@@ -226,6 +231,41 @@ class Oracle:
                                  _dt(dt))
         return out
 
+    def ids_fill(self, numRows, numBlocks):
+        ids = np.empty((numRows, numBlocks), np.int32)
+        self.L.ref_ids_fill(_p(ids), numRows, numBlocks)
+        return ids
+
+    def expand(self, sortedIds, ctx, B, S, rowStart, numRows, outIdx=None):
+        """K4: outIdx int32 [B*S, 2051]; rows outside the chunk keep `outIdx` (zeros)."""
+        sortedIds = _i32(sortedIds)
+        ctx = _i32(ctx)
+        out = np.zeros((B * S, 2051), np.int32) if outIdx is None else _i32(outIdx).copy()
+        self.L.ref_expand(_p(out), _p(sortedIds), _p(ctx), B, S, sortedIds.shape[1], rowStart,
+                          numRows)
+        return out
+
+    def topk_expand(self, logits, ctx, B, S, rowStart, numRows, outIdx=None):
+        """Prefill selection: full stable descending sort of each row, then K4.  Returns
+        (outIdx [B*S, 2051], sortedIds [numRows, numBlocks])."""
+        logits = np.ascontiguousarray(logits, np.float32)
+        ctx = _i32(ctx)
+        nb = logits.shape[1]
+        out = np.zeros((B * S, 2051), np.int32) if outIdx is None else _i32(outIdx).copy()
+        srt = np.empty((numRows, nb), np.int32)
+        self.L.ref_topk_expand(_p(out), _p(srt), _p(logits), _p(ctx), B, S, nb, rowStart,
+                               numRows)
+        return out, srt
+
+    def topk_expand_decode(self, logits, ctx):
+        """Decode selection: logits float32 [B, maxBlocks] -> outIdx int32 [B, 2051]."""
+        logits = np.ascontiguousarray(logits, np.float32)
+        ctx = _i32(ctx)
+        B, mb = logits.shape
+        out = np.empty((B, 2051), np.int32)
+        self.L.ref_topk_expand_decode(_p(out), _p(logits), _p(ctx), B, mb)
+        return out
+
     def score_scale(self):
         return self.L.ref_score_scale()
 
@@ -243,6 +283,7 @@ def default():
 def __getattr__(name):
     # module-level q_prep / k_compress / persist / widen / narrow / ... use the default build
     if name in ("q_prep", "k_compress", "persist", "widen", "narrow", "set_threads",
-                "max_threads", "pre_decode", "scores", "scores_decode", "score_scale"):
+                "max_threads", "pre_decode", "scores", "scores_decode", "score_scale", "ids_fill",
+                "expand", "topk_expand", "topk_expand_decode"):
         return getattr(default(), name)
     raise AttributeError(name)

@@ -636,4 +636,130 @@ def check_scores_decode_matches_prefill(O):
     assert np.array_equal(lg2[0, :32], lg[0, :32]) and np.array_equal(lg2[0, 64:75], lg[0, 64:75])
 
 
+# ----------------------------------------------------------------- selection + expand ----
+
+def _orderable_np(lg):
+    """The page's map u = bits >= 0 ? bits | 0x80000000 : ~bits, in numpy (int64 keys)."""
+    b = np.ascontiguousarray(lg, np.float32).view(np.uint32).astype(np.int64)
+    return np.where(b & 0x80000000, (~b) & 0xFFFFFFFF, b | 0x80000000)
+
+
+def check_expand_hand_worked(O):
+    """launchQsaIndexExpand on hand-worked rows: t=0 is only its tail token; t=3 one block; t=6
+    one block plus tail 4,5,6; t=2050 fills all 2051 slots (4*512 + 3); a padded row is -1."""
+    S = 2051
+    sorted_ids = np.tile(np.arange(512, dtype=np.int32)[::-1], (5, 1))  # any order: 511, 510, ..
+    rows = {0: [0], 3: [511 * 4 + j for j in range(4)],
+            6: [511 * 4 + j for j in range(4)] + [4, 5, 6]}
+    for t, expect in rows.items():
+        out = O.expand(sorted_ids[:1], np.array([S]), 1, S, t, 1)[t]
+        assert out[:len(expect)].tolist() == expect and np.all(out[len(expect):] == -1), t
+    out = O.expand(sorted_ids[:1], np.array([S]), 1, S, 2050, 1)[2050]
+    assert np.all(out >= 0) and out[-3:].tolist() == [2048, 2049, 2050]
+    assert sorted(out[:2048].tolist()) == list(range(2048))
+    out = O.expand(sorted_ids[:1], np.array([100]), 1, S, 100, 1)[100]
+    assert np.all(out == -1)
+
+
+def check_expand_invariants(O):
+    """Every expanded row lists distinct tokens in [0, t]: 4 per selected block, then the tail
+    [4*nVis, t]; the count is 4*min(512, nVis) + (t+1)%4."""
+    rng = np.random.default_rng(83)
+    B, S = 2, 3000
+    nb = S // 4
+    ts = rng.choice(S, 40, replace=False)
+    for t in ts:
+        nvis = (t + 1) // 4
+        srt = np.zeros((1, nb), np.int32)
+        srt[0, :nvis] = rng.permutation(nvis)
+        out = O.expand(srt, np.array([S, S]), B, S, S + int(t), 1)[S + t]
+        n = 4 * min(512, nvis) + (t + 1) % 4
+        v = out[:n]
+        assert np.all(out[n:] == -1) and len(set(v.tolist())) == n
+        assert np.all((v >= 0) & (v <= t))
+        assert v[4 * min(512, nvis):].tolist() == list(range(4 * nvis, t + 1))
+
+
+def check_orderable_map(O):
+    """The selection's key order is the float order (non-NaN), with -0 just below +0."""
+    rng = np.random.default_rng(89)
+    x = np.concatenate([rng.standard_normal(5000).astype(np.float32) * 1e3,
+                        np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45,
+                                  np.finfo(np.float32).max, -np.finfo(np.float32).max],
+                                 np.float32)])
+    # the oracle's ordering through a one-row prefill selection over all of x
+    S = 4 * len(x)
+    out, srt = O.topk_expand(x[None, :], np.array([S]), 1, S, S - 1, 1)
+    order = x[srt[0]]
+    assert np.all(order[:-1] >= order[1:])
+    pz, nz = np.where((x == 0) & ~np.signbit(x))[0][0], np.where((x == 0) & np.signbit(x))[0][0]
+    assert list(srt[0]).index(pz) < list(srt[0]).index(nz)
+    assert np.array_equal(np.argsort(-_orderable_np(x), kind="stable"), srt[0])
+
+
+def check_topk_vs_numpy(O):
+    """The prefill selection equals numpy's stable argsort of the descending keys (ties in
+    ascending id) followed by the expand rule; a padded row is -1."""
+    rng = np.random.default_rng(97)
+    B, S = 2, 2400
+    nb = S // 4
+    lg = (rng.standard_normal((B * S, nb)) ** 2).astype(np.float32)
+    lg[:, ::7] = lg[:, 3:4]             # many exact ties
+    ctx = np.array([2400, 2100], np.int32)
+    rows = np.sort(rng.choice(B * S, 64, replace=False))
+    for r in rows:
+        out, srt = O.topk_expand(lg[r:r + 1], ctx, B, S, int(r), 1)
+        ref = np.argsort(-_orderable_np(lg[r]), kind="stable")
+        assert np.array_equal(srt[0], ref)
+        b, t = divmod(int(r), S)
+        if t >= ctx[b]:
+            assert np.all(out[r] == -1)
+            continue
+        nvis = (t + 1) // 4
+        k = min(512, nvis)
+        exp = (ref[:k, None] * 4 + np.arange(4)).reshape(-1).tolist() + \
+            list(range(4 * nvis, t + 1))
+        assert out[r, :len(exp)].tolist() == exp and np.all(out[r, len(exp):] == -1)
+
+
+def check_topk_ties_and_decode_set(O):
+    """launchQsaTopKExpandDecode: equal keys at the threshold are taken in ascending block id;
+    nVis <= 512 takes every block without reading logits; the decode selection is the same
+    block set as the prefill selection of the same logits, emitted in ascending id order."""
+    rng = np.random.default_rng(101)
+    B, mb = 6, 4000
+    lg = np.full((B, mb), np.nan, np.float32)
+    ctx = np.array([4000 * 4, 2051, 513 * 4 + 2, 9, 0, 3000], np.int32)
+    for b in range(B):
+        n = max(0, min(mb, int(ctx[b]) // 4))
+        lg[b, :n] = rng.integers(0, 50, n).astype(np.float32)   # heavy ties
+    lg[1, :] = np.nan                                            # nVis = 512: never read
+    out = O.topk_expand_decode(lg, ctx)
+    for b in range(B):
+        c = int(ctx[b])
+        if c <= 0:
+            assert np.all(out[b] == -1)
+            continue
+        nvis = min(mb, c // 4)
+        k = min(512, nvis)
+        sel = out[b, :4 * k:4] // 4
+        assert np.all(np.diff(sel) > 0)                          # ascending id order
+        assert out[b, 4 * k:4 * k + c % 4].tolist() == list(range(4 * nvis, 4 * nvis + c % 4))
+        if nvis <= 512:
+            assert sel.tolist() == list(range(nvis))
+            continue
+        key = _orderable_np(lg[b, :nvis])
+        thr = np.sort(key)[::-1][k - 1]
+        assert np.all(key[sel] >= thr) and np.sum(key > thr) <= k
+        eq = np.where(key == thr)[0]
+        need = k - int(np.sum(key > thr))
+        assert np.array_equal(np.intersect1d(sel, eq), eq[:need])   # ascending id at the tie
+        # same set as the prefill selection of row t = c - 1 with the same logits
+        S = c
+        row = np.full((1, nvis), 0, np.float32)
+        row[0] = lg[b, :nvis]
+        pout, _ = O.topk_expand(row, np.array([S]), 1, S, S - 1, 1)
+        assert set(pout[S - 1, :4 * k].tolist()) == set(out[b, :4 * k].tolist())
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

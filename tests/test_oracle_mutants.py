@@ -55,6 +55,17 @@ MUTANTS = {
     "score_padding_rule": ("if (c <= 0 || t >= c) {", "if (c <= 0 || t > c) {"),
     "score_decode_plane": ("int64_t off = pool_tail_offset(pool, b, 1, 4 * g);\n      logits",
                            "int64_t off = pool_tail_offset(pool, b, 0, 4 * g);\n      logits"),
+    "expand_no_tail": ("  for (int64_t j = 0; j < tail; ++j) out[n++] = (int32_t)(4 * nVis + j);\n  while",
+                       "  (void)tail;\n  while"),
+    "topk_511": ("enum { TOPK = 512, INDEX_WIDTH = 2051 };", "enum { TOPK = 511, INDEX_WIDTH = 2051 };"),
+    "ties_descending_id": ("return a->id < b->id ? -1 : (a->id > b->id);",
+                           "return a->id > b->id ? -1 : (a->id < b->id);"),
+    "orderable_negatives_uncomplemented": ("return (b & 0x80000000u) ? ~b : (b | 0x80000000u);",
+                                           "return (b & 0x80000000u) ? (b & 0x7fffffffu) : (b | 0x80000000u);"),
+    "decode_emits_sorted_order": ("      for (int64_t g = 0; g < nVis; ++g)\n        if (pick[g]) sel[n++] = (int32_t)g;",
+                                  "      for (int64_t i = 0; i < kSel; ++i) sel[n++] = kv[i].id;"),
+    "expand_padded_rule": ("    if (ctx[b] <= 0 || t >= ctx[b]) {\n      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;\n      continue;\n    }\n    int64_t nVis = (t + 1) / 4;\n    expand_row(out, sortedIds",
+                           "    if (ctx[b] <= 0 || t > ctx[b]) {\n      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;\n      continue;\n    }\n    int64_t nVis = (t + 1) / 4;\n    expand_row(out, sortedIds"),
     "rsqrt_single": ("float inv = (float)(1.0 / sqrt((double)v));",
                      "float inv = 1.0f / (float)sqrt((double)v) * (1.0f + 1.2e-7f);"),
 }
