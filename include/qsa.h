@@ -60,6 +60,8 @@ enum {
 #define QSA_COMPRESS_RATIO 4   /* tokens per compressed block                             */
 #define QSA_PAGE_TOKENS 128    /* tokens per pool page                                    */
 #define QSA_UNUSED_PAGE_ENTRY (-1)
+#define QSA_TOPK 512           /* blocks a query selects at most                          */
+#define QSA_INDEX_WIDTH 2051   /* token indices per query row: 4 * QSA_TOPK + 3 tail slots  */
 
 /*
  * Where the indexer state lives ("Qsa Indexer Kernels": struct QsaIndexerPoolState).
@@ -245,6 +247,60 @@ int qsa_index_scores(float* logits, const void* qNormed, const void* kbar,
 int qsa_index_scores_decode(float* logits, const void* qNormed, const int32_t* contextLengths,
                             const qsa_pool_state_t* pool, int32_t batchSize, int32_t maxBlocks,
                             qsa_dtype dt, void* stream);
+
+/*
+ * Block selection and expansion to token indices ("Qsa Indexer Kernels": launchQsaIndexIdsFill,
+ * launchQsaIndexExpand, launchQsaTopKExpandDecode).  All integer; results are exact.
+ *
+ * Keys: a logit's FP32 bits mapped monotonically to u = bits >= 0 ? bits | 0x80000000 : ~bits;
+ * a row is ordered by descending u, equal u by ascending block id (the order of a stable
+ * descending sort over ascending ids).  For a query row with t = its position and
+ * nVis = (t+1)/4 complete blocks, kSel = min(512, nVis): out[4i + j] = id_i * 4 + j for i < kSel,
+ * j < 4, then the tail tokens out[4*kSel + j] = 4*nVis + j for j < (t+1) % 4, then -1 up to
+ * QSA_INDEX_WIDTH.  A padded row (t >= ctx[b], or ctx[b] <= 0) is -1 throughout.
+ */
+
+/* ids [out] device int32 [numRows, numBlocks]: ids[r][c] = c. */
+int qsa_index_ids_fill(int32_t* ids, int32_t numRows, int32_t numBlocks, void* stream);
+
+/*
+ * K4 over global rows r = rowStart + i = b*S + t, i < numRows.
+ * outIdx    [out] device int32 [B*S, QSA_INDEX_WIDTH]; only the chunk's rows are written.
+ * sortedIds [in]  device int32 [numRows, numBlocks]: each row's block ids in selection order;
+ *                 only the first kSel entries are read.  numBlocks >= min(512, seqLen/4).
+ */
+int qsa_index_expand(int32_t* outIdx, const int32_t* sortedIds, const int32_t* contextLengths,
+                     int32_t batchSize, int32_t seqLen, int32_t numBlocks, int32_t rowStart,
+                     int32_t numRows, void* stream);
+
+/*
+ * Prefill selection + K4 in one pass (the page's ids fill, per-row descending sort and expand,
+ * without materialising the sorted rows).
+ * logits [in] device FP32 [numRows, numBlocks] (the layout qsa_index_scores writes).
+ * Row i selects the kSel largest keys among its complete blocks [0, min(nVis, numBlocks)) and
+ * emits them in descending key order, equal keys by ascending id.  This is the page's full-row
+ * sort whenever no logit past a row's complete blocks outranks a selected one, which holds for
+ * logits from qsa_index_scores (complete blocks >= 0, the rest -FLT_MAX); entries past the
+ * complete blocks are not read.
+ */
+int qsa_index_topk_expand(int32_t* outIdx, const float* logits, const int32_t* contextLengths,
+                          int32_t batchSize, int32_t seqLen, int32_t numBlocks, int32_t rowStart,
+                          int32_t numRows, void* stream);
+
+/*
+ * Decode selection + expand, one query per sequence (launchQsaTopKExpandDecode).
+ * outIdx [out] device int32 [B, QSA_INDEX_WIDTH];  logits [in] device FP32 [B, maxBlocks]
+ * (qsa_index_scores_decode);  splitCounters [out, nullable] device int32 [B, numKVHeads]: the
+ * split-merge counters of the decode attention that follows, zeroed here when non-NULL.
+ * nVis = ctx/4, which maxBlocks must cover (a larger ctx is capped: nVis = maxBlocks, the tail
+ * tokens then start at 4*maxBlocks); tail = ctx % 4.  nVis <= 512 takes every block 0..nVis-1
+ * and reads no logits.  Otherwise the kSel = 512 largest keys of [0, nVis), equal keys at the
+ * threshold in ascending id, emitted in ascending block id.  ctx <= 0 gives an all -1 row.
+ */
+int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits,
+                                 const int32_t* contextLengths, int32_t* splitCounters,
+                                 int32_t numKVHeads, int32_t batchSize, int32_t maxBlocks,
+                                 void* stream);
 
 /*
  * Debug forms: the same kernels with their FP32 intermediates written out.  Arguments as the

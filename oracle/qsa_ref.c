@@ -594,19 +594,23 @@ void ref_topk_expand(int32_t* outIdx, int32_t* sortedIds /*nullable*/, const flo
 }
 
 /*
- * launchQsaTopKExpandDecode (without the split counters, which belong to the attention
- * kernel): per sequence, nVis = ctx/4 (capped at maxBlocks), kSel = min(512, nVis),
+ * launchQsaTopKExpandDecode: per sequence, the split counters splitCounters[b][0, numKVHeads)
+ * of the attention that follows are zeroed when the pointer is non-null (step a.); then
+ * nVis = ctx/4 (capped at maxBlocks), kSel = min(512, nVis),
  * tail = ctx%4.  nVis <= 512 selects every block.  Otherwise the selected set is the kSel
  * largest orderable keys of logits[b][0, nVis), equal keys at the threshold taken in ascending
  * block id; the selection is emitted in ascending block id order (a fixed-order scan), expanded
  * to 4 tokens each, followed by the tail tokens [4*nVis, ctx) and -1 padding to 2051.
  * ctx <= 0 gives an all -1 row.
  */
-void ref_topk_expand_decode(int32_t* outIdx, const float* logits, const int32_t* ctx, int32_t B,
+void ref_topk_expand_decode(int32_t* outIdx, const float* logits, const int32_t* ctx,
+                            int32_t* splitCounters, int32_t numKVHeads, int32_t B,
                             int32_t maxBlocks) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t b = 0; b < B; ++b) {
     int32_t* out = outIdx + b * INDEX_WIDTH;
+    if (splitCounters)
+      for (int64_t h = 0; h < numKVHeads; ++h) splitCounters[b * numKVHeads + h] = 0;
     int64_t c = ctx[b];
     if (c <= 0) {
       for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;

@@ -93,7 +93,7 @@ class Oracle:
         L.ref_ids_fill.argtypes = [P, I32, I32]
         L.ref_expand.argtypes = [P, P, P, I32, I32, I32, I32, I32]
         L.ref_topk_expand.argtypes = [P, P, P, P, I32, I32, I32, I32, I32]
-        L.ref_topk_expand_decode.argtypes = [P, P, P, I32, I32]
+        L.ref_topk_expand_decode.argtypes = [P, P, P, P, I32, I32, I32]
         L.ref_widen.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_narrow.argtypes = [P, P, I64, ctypes.c_int]
         L.ref_set_threads.argtypes = [ctypes.c_int]
@@ -257,14 +257,18 @@ class Oracle:
                                numRows)
         return out, srt
 
-    def topk_expand_decode(self, logits, ctx):
-        """Decode selection: logits float32 [B, maxBlocks] -> outIdx int32 [B, 2051]."""
+    def topk_expand_decode(self, logits, ctx, splitCounters=None):
+        """Decode selection: logits float32 [B, maxBlocks] -> outIdx int32 [B, 2051]; with
+        splitCounters int32 [B, numKVHeads] given, returns (outIdx, the counters after)."""
         logits = np.ascontiguousarray(logits, np.float32)
         ctx = _i32(ctx)
         B, mb = logits.shape
         out = np.empty((B, 2051), np.int32)
-        self.L.ref_topk_expand_decode(_p(out), _p(logits), _p(ctx), B, mb)
-        return out
+        sc = None if splitCounters is None else _i32(splitCounters).copy()
+        self.L.ref_topk_expand_decode(_p(out), _p(logits), _p(ctx),
+                                      None if sc is None else _p(sc),
+                                      0 if sc is None else sc.shape[1], B, mb)
+        return out if sc is None else (out, sc)
 
     def score_scale(self):
         return self.L.ref_score_scale()

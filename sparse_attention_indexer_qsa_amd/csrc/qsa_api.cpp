@@ -54,8 +54,9 @@ int check_eps(float eps) {
   return QSA_OK;
 }
 
+// Every kernel runs 256-thread workgroups; a launch's x extent counts work-items in 32 bits.
 int check_grid(int64_t workgroups) {
-  if (workgroups > INT_MAX)
+  if (workgroups > (int64_t)(UINT32_MAX / 256u))
     return fail(QSA_E_INVALID, "problem needs %lld workgroups, more than one launch can hold",
                 (long long)workgroups);
   return QSA_OK;
@@ -381,6 +382,90 @@ QSA_EXPORT int qsa_index_scores_decode(float* logits, const void* qNormed,
   (void)hipGetLastError();
   return launched(qsa::launch_scores_decode(a, t, static_cast<hipStream_t>(stream)),
                   "qsa_index_scores_decode");
+}
+
+namespace {
+
+// Row chunk [rowStart, rowStart + numRows) of a [B*S, ...] problem.
+int check_rows(int32_t B, int32_t S, int32_t numBlocks, int32_t rowStart, int32_t numRows) {
+  if (B < 0 || S < 0 || numBlocks < 0 || rowStart < 0 || numRows < 0)
+    return fail(QSA_E_INVALID, "batchSize = %d, seqLen = %d, numBlocks = %d, rowStart = %d, "
+                "numRows = %d must be >= 0", B, S, numBlocks, rowStart, numRows);
+  if ((int64_t)rowStart + numRows > (int64_t)B * S)
+    return fail(QSA_E_INVALID, "rowStart + numRows = %lld > batchSize * seqLen = %lld",
+                (long long)rowStart + numRows, (long long)B * S);
+  return QSA_OK;
+}
+
+}  // namespace
+
+QSA_EXPORT int qsa_index_ids_fill(int32_t* ids, int32_t numRows, int32_t numBlocks,
+                                  void* stream) {
+  if (numRows < 0 || numBlocks < 0)
+    return fail(QSA_E_INVALID, "numRows = %d, numBlocks = %d must be >= 0", numRows, numBlocks);
+  if (numRows == 0 || numBlocks == 0) return ok();
+  TRY(need(ids, "ids", 4));
+  (void)hipGetLastError();
+  return launched(qsa::launch_ids_fill(ids, (int64_t)numRows * numBlocks, numBlocks,
+                                       static_cast<hipStream_t>(stream)),
+                  "qsa_index_ids_fill");
+}
+
+QSA_EXPORT int qsa_index_expand(int32_t* outIdx, const int32_t* sortedIds,
+                                const int32_t* contextLengths, int32_t batchSize, int32_t seqLen,
+                                int32_t numBlocks, int32_t rowStart, int32_t numRows,
+                                void* stream) {
+  TRY(check_rows(batchSize, seqLen, numBlocks, rowStart, numRows));
+  if (numRows == 0) return ok();
+  const int32_t maxSel = seqLen / 4 < QSA_TOPK ? seqLen / 4 : QSA_TOPK;
+  if (numBlocks < maxSel)
+    return fail(QSA_E_INVALID, "numBlocks = %d < min(%d, seqLen/4) = %d: a row would need "
+                "more sorted ids than it holds", numBlocks, QSA_TOPK, maxSel);
+  TRY(need(outIdx, "outIdx", 4));
+  if (maxSel > 0) TRY(need(sortedIds, "sortedIds", 4));
+  TRY(need(contextLengths, "contextLengths", 4));
+  TRY(check_grid(numRows));
+  const qsa::ExpandArgs a{outIdx, sortedIds, contextLengths, seqLen, numBlocks, rowStart, numRows};
+  (void)hipGetLastError();
+  return launched(qsa::launch_expand(a, static_cast<hipStream_t>(stream)), "qsa_index_expand");
+}
+
+QSA_EXPORT int qsa_index_topk_expand(int32_t* outIdx, const float* logits,
+                                     const int32_t* contextLengths, int32_t batchSize,
+                                     int32_t seqLen, int32_t numBlocks, int32_t rowStart,
+                                     int32_t numRows, void* stream) {
+  TRY(check_rows(batchSize, seqLen, numBlocks, rowStart, numRows));
+  if (numRows == 0) return ok();
+  TRY(need(outIdx, "outIdx", 4));
+  if (numBlocks > 0) TRY(need(logits, "logits", 4));
+  TRY(need(contextLengths, "contextLengths", 4));
+  TRY(check_grid(numRows));
+  const qsa::TopkArgs a{outIdx, logits, contextLengths, seqLen, numBlocks, rowStart, numRows};
+  (void)hipGetLastError();
+  return launched(qsa::launch_topk_expand(a, static_cast<hipStream_t>(stream)),
+                  "qsa_index_topk_expand");
+}
+
+QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits,
+                                            const int32_t* contextLengths,
+                                            int32_t* splitCounters, int32_t numKVHeads,
+                                            int32_t batchSize, int32_t maxBlocks, void* stream) {
+  if (batchSize < 0 || maxBlocks < 0)
+    return fail(QSA_E_INVALID, "batchSize = %d, maxBlocks = %d must be >= 0", batchSize,
+                maxBlocks);
+  if (splitCounters != nullptr && numKVHeads < 0)
+    return fail(QSA_E_INVALID, "numKVHeads = %d must be >= 0", numKVHeads);
+  if (batchSize == 0) return ok();
+  TRY(need(outIdx, "outIdx", 4));
+  if (splitCounters != nullptr) TRY(need(splitCounters, "splitCounters", 4));
+  if (maxBlocks > QSA_TOPK) TRY(need(logits, "logits", 4));
+  TRY(need(contextLengths, "contextLengths", 4));
+  TRY(check_grid(batchSize));
+  const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
+                              splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
+  (void)hipGetLastError();
+  return launched(qsa::launch_topk_expand_decode(a, static_cast<hipStream_t>(stream)),
+                  "qsa_index_topk_expand_decode");
 }
 
 QSA_EXPORT const char* qsa_last_error(void) { return g_err; }

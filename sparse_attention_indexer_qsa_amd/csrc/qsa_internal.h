@@ -1,5 +1,5 @@
 // qsa_internal.h — argument blocks and launchers shared by the ABI layer (qsa_api.cpp) and
-// the kernels (qsa_kernels.hip).  Not part of the public ABI; see include/qsa.h.
+// the kernels (qsa_kernels.hip, qsa_scores.hip, qsa_select.hip).  Not part of the public ABI; see include/qsa.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -114,6 +114,33 @@ struct ScoresDecodeArgs {
   int32_t B, maxBlocks;
 };
 
+// K4 over rows [rowStart, rowStart + numRows); sortedIds is [numRows, numBlocks].
+struct ExpandArgs {
+  int32_t* outIdx;
+  const int32_t* sortedIds;
+  const int32_t* ctx;
+  int32_t S, numBlocks;
+  int64_t rowStart, numRows;
+};
+
+// Prefill selection + K4 over rows [rowStart, rowStart + numRows); logits is [numRows, numBlocks].
+struct TopkArgs {
+  int32_t* outIdx;
+  const float* logits;
+  const int32_t* ctx;
+  int32_t S, numBlocks;
+  int64_t rowStart, numRows;
+};
+
+struct TopkDecodeArgs {
+  int32_t* outIdx;
+  const float* logits;
+  const int32_t* ctx;
+  int32_t* splitCounters;  // nullable: [B, numKVHeads] zeroed
+  int32_t numKVHeads;
+  int32_t B, maxBlocks;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.  Arguments are already validated.
 hipError_t launch_q_prep(const QPrepArgs& a, Dt dt, bool debug, hipStream_t stream);
 hipError_t launch_k_compress(const KCompressArgs& a, Dt dt, bool debug, hipStream_t stream);
@@ -122,5 +149,9 @@ hipError_t launch_prefill(const PrefillArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_pre_decode(const PreDecodeArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream);
+hipError_t launch_ids_fill(int32_t* ids, int64_t total, int32_t numBlocks, hipStream_t stream);
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream);
+hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream);
 
 }  // namespace qsa

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 QSA_F16, QSA_BF16 = 0, 1
 QSA_OK, QSA_E_INVALID, QSA_E_ALIGN, QSA_E_DTYPE, QSA_E_LAUNCH = 0, -1, -2, -3, -4
 ROW_WIDTH, HEAD_DIM, HEADS = 640, 128, 4
+TOPK, INDEX_WIDTH = 512, 2051
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
@@ -52,6 +53,10 @@ def _declare(lib):
         "qsa_index_pre_decode": [P, P, P, I, P, P, P, P, F, P, I, I, ctypes.c_int, P],
         "qsa_index_scores": [P, P, P, P, I, I, I, I, I, ctypes.c_int, P],
         "qsa_index_scores_decode": [P, P, P, P, I, I, ctypes.c_int, P],
+        "qsa_index_ids_fill": [P, I, I, P],
+        "qsa_index_expand": [P, P, P, I, I, I, I, I, P],
+        "qsa_index_topk_expand": [P, P, P, I, I, I, I, I, P],
+        "qsa_index_topk_expand_decode": [P, P, P, P, I, I, I, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -288,6 +293,56 @@ def qsa_index_scores_decode(logits, qNormed, contextLengths, pool, maxBlocks, ba
                                        _dev(contextLengths, "contextLengths", B, _I32),
                                        ctypes.byref(pool.c_struct(B)), B, maxBlocks,
                                        _dt_of(qNormed, dt), _stream(stream)))
+
+
+def qsa_index_ids_fill(ids, numRows, numBlocks, stream=None):
+    """ids int32 [numRows, numBlocks]: ids[r][c] = c."""
+    if numRows == 0 or numBlocks == 0:
+        return
+    _check(lib.qsa_index_ids_fill(_dev(ids, "ids", numRows * numBlocks, _I32), numRows,
+                                  numBlocks, _stream(stream)))
+
+
+def qsa_index_expand(outIdx, sortedIds, contextLengths, batchSize, seqLen, numBlocks, rowStart,
+                     numRows, stream=None):
+    """K4: rows [rowStart, rowStart+numRows) of outIdx int32 [B*S, 2051] from sortedIds int32
+    [numRows, numBlocks]."""
+    if numRows == 0:
+        return
+    _check(lib.qsa_index_expand(
+        _dev(outIdx, "outIdx", batchSize * seqLen * INDEX_WIDTH, _I32),
+        _dev(sortedIds, "sortedIds", numRows * numBlocks, _I32) if numBlocks else None,
+        _dev(contextLengths, "contextLengths", batchSize, _I32), batchSize, seqLen, numBlocks,
+        rowStart, numRows, _stream(stream)))
+
+
+def qsa_index_topk_expand(outIdx, logits, contextLengths, batchSize, seqLen, numBlocks,
+                          rowStart, numRows, stream=None):
+    """Prefill top-512 selection + K4: rows [rowStart, rowStart+numRows) of outIdx int32
+    [B*S, 2051] from logits FP32 [numRows, numBlocks]."""
+    if numRows == 0:
+        return
+    _check(lib.qsa_index_topk_expand(
+        _dev(outIdx, "outIdx", batchSize * seqLen * INDEX_WIDTH, _I32),
+        _dev(logits, "logits", numRows * numBlocks, _F32) if numBlocks else None,
+        _dev(contextLengths, "contextLengths", batchSize, _I32), batchSize, seqLen, numBlocks,
+        rowStart, numRows, _stream(stream)))
+
+
+def qsa_index_topk_expand_decode(outIdx, logits, contextLengths, maxBlocks, splitCounters=None,
+                                 numKVHeads=0, batchSize=None, stream=None):
+    """Decode top-512 selection + expand: outIdx int32 [B, 2051] from logits FP32
+    [B, maxBlocks]; splitCounters int32 [B, numKVHeads] zeroed when given."""
+    B = contextLengths.shape[0] if batchSize is None else batchSize
+    if B == 0:
+        return
+    _check(lib.qsa_index_topk_expand_decode(
+        _dev(outIdx, "outIdx", B * INDEX_WIDTH, _I32),
+        _dev(logits, "logits", B * maxBlocks, _F32) if maxBlocks > TOPK else None,
+        _dev(contextLengths, "contextLengths", B, _I32),
+        None if splitCounters is None else _dev(splitCounters, "splitCounters",
+                                                B * numKVHeads, _I32),
+        numKVHeads, B, maxBlocks, _stream(stream)))
 
 
 def qsa_last_error():

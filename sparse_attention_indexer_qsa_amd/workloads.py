@@ -226,5 +226,62 @@ def config5(B=32, S=8192, numPages=8192):
                     0, nb, 0, PoolSpec(numPages, pt), subcalls=subcalls)
 
 
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def _logit_values(rng, n, style):
+    """n FP32 logits in a style: "scores" (non-negative, a ReLU's share of exact zeros, coarse
+    quantisation so that equal values recur), "ties" (few distinct values), "normal"
+    (both signs, continuous), "special" (normal plus +-0, subnormals, +-inf, NaNs of both signs,
+    +-FLT_MAX), "special_ge" (as "special" without the values below -FLT_MAX: -inf and NaNs
+    with the sign bit set)."""
+    if style == "scores":
+        v = np.maximum(rng.standard_normal(n) * 2.0, 0.0)
+        return (np.round(v * 64.0) / 64.0).astype(np.float32)
+    if style == "ties":
+        return rng.integers(0, 4, n).astype(np.float32) * np.float32(0.5)
+    v = rng.standard_normal(n).astype(np.float32)
+    if style in ("special", "special_ge"):
+        low = style == "special"
+        specials = np.array([0.0, -0.0, 1e-45, -1e-45, np.inf, -FLT_MAX, FLT_MAX]
+                            + ([-np.inf] if low else []), np.float32)
+        pick = rng.random(n) < 0.05
+        v[pick] = specials[rng.integers(0, len(specials), int(pick.sum()))]
+        nan = rng.random(n) < 0.01
+        neg = (rng.random(n) < 0.5) & low
+        bits = np.where(neg, 0xFFC00001, 0x7FC00000).astype(np.uint32)
+        v.view(np.uint32)[nan] = bits[nan]
+    return v
+
+
+def prefill_logits(seed, ctx, S, numBlocks, rowStart, numRows, styles=("scores",)):
+    """Logits FP32 [numRows, numBlocks] laid out as the block scores of rows [rowStart,
+    rowStart+numRows) are: row r = b*S + t has its first (t+1)//4 entries (capped at numBlocks)
+    drawn in one of `styles` (cycled by row), the rest -FLT_MAX; padded rows (t >= ctx[b])
+    are -FLT_MAX throughout."""
+    rng = np.random.default_rng(seed)
+    out = np.full((numRows, numBlocks), -FLT_MAX, np.float32)
+    for i in range(numRows):
+        r = rowStart + i
+        b, t = divmod(r, S)
+        if t >= ctx[b]:
+            continue
+        n = min((t + 1) // 4, numBlocks)
+        out[i, :n] = _logit_values(rng, n, styles[i % len(styles)])
+    return out
+
+
+def decode_logits(seed, ctx, maxBlocks, styles=("scores", "ties", "normal", "special")):
+    """Logits FP32 [B, maxBlocks] of one decode step: the first min(ctx/4, maxBlocks) entries of
+    sequence b drawn in styles[b % len(styles)], the rest left NaN (never read)."""
+    rng = np.random.default_rng(seed)
+    B = len(ctx)
+    out = np.full((B, maxBlocks), np.nan, np.float32)
+    for b in range(B):
+        n = max(0, min(int(ctx[b]) // 4, maxBlocks))
+        out[b, :n] = _logit_values(rng, n, styles[b % len(styles)])
+    return out
+
+
 def make(n, **kw):
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)

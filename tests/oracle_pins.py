@@ -735,6 +735,8 @@ def check_topk_ties_and_decode_set(O):
         lg[b, :n] = rng.integers(0, 50, n).astype(np.float32)   # heavy ties
     lg[1, :] = np.nan                                            # nVis = 512: never read
     out = O.topk_expand_decode(lg, ctx)
+    out2, sc = O.topk_expand_decode(lg, ctx, np.full((B, 3), 7, np.int32))
+    assert np.array_equal(out2, out) and np.all(sc == 0)         # step a.: counters zeroed
     for b in range(B):
         c = int(ctx[b])
         if c <= 0:
