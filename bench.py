@@ -137,6 +137,68 @@ def decode_leg(qsa, torch, steps, warmup):
             "blocks_compressed_per_call": blocks}
 
 
+def _time_stream(torch, fn, steps, warmup):
+    """Average microseconds per call of fn() on a fresh stream, timed with stream events."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn(stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn(stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=65536):
+    """Top-512 selection + expand (qsa_index_topk_expand) of the long-prefill rows whose block
+    scores the scores leg produced.  Reads each row's complete blocks, writes 2051 indices."""
+    import numpy as np
+    S, nb = wl.S, wl.numBlocks
+    numRows = logits.shape[0]
+    out = torch.empty(S, qsa.INDEX_WIDTH, dtype=torch.int32, device="cuda")
+    ctx = torch.tensor([S], dtype=torch.int32, device="cuda")
+
+    def call(st):
+        rc = qsa.lib.qsa_index_topk_expand(out.data_ptr(), logits.data_ptr(), ctx.data_ptr(), 1,
+                                           S, nb, rowStart, numRows, st)
+        assert rc == 0, qsa.qsa_last_error()
+    us = _time_stream(torch, call, steps, warmup)
+    t = rowStart + np.arange(numRows)
+    visible = int(np.minimum((t + 1) // 4, nb).sum())
+    alg = 4 * visible + 4 * qsa.INDEX_WIDTH * numRows
+    del out
+    return {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks",
+            "entry": "qsa_index_topk_expand", "us_per_call": us, "alg_bytes": alg,
+            "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS}
+
+
+def select_decode_leg(qsa, torch, steps, warmup):
+    """Decode top-512 selection + expand (qsa_index_topk_expand_decode) for the decode
+    workload's 64 sequences (context lengths up to 32772, scores-like logits)."""
+    import numpy as np
+    from sparse_attention_indexer_qsa_amd import workloads as W
+    wl = W.config4()
+    ctx = (wl.ranges[0] + 1).astype(np.int32)
+    mb = int((ctx.max() + 3) // 4)
+    lg = torch.from_numpy(W.decode_logits(5, ctx, mb, styles=("scores",))).cuda()
+    c = torch.from_numpy(ctx).cuda()
+    out = torch.empty(len(ctx), qsa.INDEX_WIDTH, dtype=torch.int32, device="cuda")
+
+    def call(st):
+        rc = qsa.lib.qsa_index_topk_expand_decode(out.data_ptr(), lg.data_ptr(), c.data_ptr(),
+                                                  None, 0, len(ctx), mb, st)
+        assert rc == 0, qsa.qsa_last_error()
+    us = _time_stream(torch, call, steps, warmup)
+    alg = 4 * int(np.minimum(ctx // 4, mb)[ctx // 4 > 512].sum()) + 4 * qsa.INDEX_WIDTH * len(ctx)
+    return {"workload": f"decode, B={len(ctx)}, context up to {int(ctx.max())}",
+            "entry": "qsa_index_topk_expand_decode", "us_per_call": us, "alg_bytes": alg,
+            "GBps": alg / us / 1e3}
+
+
 def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=65536, numRows=8192):
     """Block scores (qsa_index_scores, MFMA) over a chunk of the long prefill's query rows,
     on the qNormed and kbar the fused prefill produced.  Bound by the FP32 logits it writes."""
@@ -162,8 +224,7 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=65536, numRows=8192):
     nvis_max = int(min((rowStart + numRows) // 4, nb))
     alg = 4 * numRows * nb + 1024 * numRows + 256 * nvis_max
     flops = 2 * 4 * 128 * visible
-    del logits
-    return {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks, "
+    return logits, {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks, "
                         f"bf16, FP32 logits", "entry": "qsa_index_scores", "us_per_call": us,
             "alg_bytes": alg, "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS,
             "visible_scores": visible, "TFLOPs": flops / us / 1e6,
@@ -385,10 +446,15 @@ def main():
             torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
 
-    scores = None
+    scores = select = select_decode = None
     if not args.no_scores:
         print("[bench] timing the block scores", file=sys.stderr, flush=True)
-        scores = scores_leg(qsa, torch, sets[0], wl, min(args.steps, 50), min(args.warmup, 5))
+        logits, scores = scores_leg(qsa, torch, sets[0], wl, min(args.steps, 50),
+                                    min(args.warmup, 5))
+        print("[bench] timing the top-512 selection", file=sys.stderr, flush=True)
+        select = select_leg(qsa, torch, wl, logits, min(args.steps, 50), min(args.warmup, 5))
+        del logits
+        select_decode = select_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
     decode = None
     if not args.no_decode:
         print("[bench] timing the decode pre-pass", file=sys.stderr, flush=True)
@@ -422,6 +488,8 @@ def main():
         "three_call": three,
         "decode_pre_pass": decode,
         "scores": scores,
+        "select": select,
+        "select_decode": select_decode,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
