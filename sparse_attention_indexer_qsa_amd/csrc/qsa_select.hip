@@ -3,20 +3,40 @@
 // "Qsa Indexer Kernels": launchQsaIndexIdsFill, launchQsaIndexExpand (K4) and
 // launchQsaTopKExpandDecode (B3).  The page's prefill selection is ids fill + a stable
 // descending segmented radix sort of every row + K4 over the first kSel = min(512, nVis)
-// entries; here it is one kernel per row that finds the kSel largest keys by radix select and
-// sorts only those, which gives the same first kSel ids in the same order.
+// entries; here one kernel per row finds the kSel largest keys and sorts only those, which
+// gives the same first kSel ids in the same order.
 //
-//  * Keys are the monotone map of the FP32 bits, u = bits >= 0 ? bits | 0x80000000 : ~bits; a
-//    row's order is descending u, equal u in ascending block id (the stable sort's order).
-//  * Radix select, MSB first, four 8-bit digits: per pass each wave histograms the digit of
-//    the keys that match the prefix found so far (LDS atomics into its own 256 bins), a block
-//    suffix scan over the bins finds the digit of the kSel-th largest key.  After four passes
-//    the threshold key T is known with the number `need` of keys equal to T that are taken.
-//  * Compaction in ascending id: 256 ids per step, wave ballots give each lane its rank among
-//    keys equal to T and its output position.  Decode writes the expansion directly (its
-//    selection is emitted in ascending id); prefill collects the <= 512 (key, id) pairs in
-//    LDS and sorts them by a bitonic network before expanding.
-//  * One workgroup of 256 threads per row; the row's keys are re-read from L2 on every pass.
+// Keys are the monotone map of the FP32 bits, u = bits >= 0 ? bits | 0x80000000 : ~bits; a
+// row's order is descending u, equal u in ascending block id (the stable sort's order).
+//
+// Register-resident rows (up to 64 keys per thread x 512 threads = 32768 blocks):
+//  * The row is read from HBM once, 16 bytes per lane, into registers.  Thread t holds the
+//    ids ((g * 512 + t) * 4 + e) for its register groups g and e < 4.
+//  * Padding: registers past the row hold u = 0 with ids >= n.  In the (u desc, id asc)
+//    order every padding key comes after every real key, so while kSel <= n the kSel first
+//    keys of the padded row are those of the row, and no step needs to tell them apart.
+//  * Window: once n >= 2048 every thread holds real keys, and the smallest of the 512
+//    per-thread maxima, lo, has at least 512 keys at or above it (shorter rows take lo = the
+//    row minimum); with hi the row maximum, the kSel-th largest key lies in [lo, hi].
+//  * Radix select inside the window, MSB first: each pass histograms (LDS atomics, 256 bins)
+//    only the keys inside the current window, at a shift that spreads the window over the 256
+//    bins, and a one-wave suffix scan picks the bin holding the kSel-th largest.  The window
+//    keeps only the top few percent of a row, so the bins are spread and the atomics rarely
+//    collide.  After the first pass the keys at or above the chosen bin (a few hundred) are
+//    compacted into LDS and the later passes run on them alone.  The result is the threshold
+//    key T, the number `need` of keys equal to T that are taken (ascending id) and their
+//    count `ties`.
+//  * Prefill: the keys >= T (kSel - need + ties of them; ties normally = need) are gathered as
+//    64-bit (u, ~id) composites and sorted descending by a bitonic network (strides < 64 by
+//    lane shuffles, 64..256 through LDS), so equal keys come out in ascending id and the first
+//    kSel are the result.  More than 1024 such keys (many equal keys at T) take the ordered
+//    path below, then the same sort.
+//  * Decode: the selection is emitted in ascending id: one block scan per register group
+//    counts, for each key, the keys above T and the keys equal to T with smaller ids.
+//
+// Rows longer than 32768 blocks use the streaming kernels at the end of the file (the same
+// radix select with 8-bit digits over the whole key range, the row re-read from L2 on every
+// pass), 256 threads per row.
 
 #include <float.h>
 
@@ -27,12 +47,452 @@ namespace {
 
 constexpr int kTopK = 512;
 constexpr int kIndexWidth = 2051;   // 4 * 512 + 3
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 256;    // streaming kernels
+constexpr int kRT = 512;            // register-resident kernels: threads per row
+constexpr int kRW = kRT / 64;       // waves per row
+constexpr int kCandCap = 2048;      // keys kept in LDS after the first radix pass
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t orderable(float f) {
   const uint32_t b = __float_as_uint(f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
+
+__device__ __forceinline__ uint32_t orderable_bits(uint32_t b) {
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ void write_tail_and_pad(int* out, int from, int64_t nVis, int tail,
+                                                   int nthreads) {
+  for (int s = from + (int)threadIdx.x; s < kIndexWidth; s += nthreads)
+    out[s] = s - from < tail ? (int)(4 * nVis + (s - from)) : -1;
+}
+
+// ------------------------------------------------------------------ register-resident ---
+
+struct RegShared {
+  int hist[256];
+  int wcnt[2][kRW];          // per-wave counts (double-buffered by caller's parity)
+  uint32_t red[2][kRW];      // per-wave max / min
+  int found[2];              // chosen bin, keys above it
+  uint32_t candU[kCandCap];
+  int32_t candId[kCandCap];
+  uint64_t sortBuf[2 * kTopK];
+  int32_t selId[kTopK];
+};
+
+__device__ __forceinline__ int key_id(int r, int tid) { return (((r >> 2) * kRT + tid) << 2) + (r & 3); }
+
+__device__ __forceinline__ uint64_t composite(uint32_t u, int id) {
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((unsigned)v, m), hi = __shfl_xor((unsigned)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int KPT>
+__device__ __forceinline__ void load_keys(const float* row, int n, bool vec, uint32_t (&u)[KPT]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int g = 0; g < KPT / 4; ++g) {
+    const int base = (g * kRT + tid) * 4;
+    if (vec && base + 4 <= n) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + base));
+      u[4 * g + 0] = orderable_bits(v.x);
+      u[4 * g + 1] = orderable_bits(v.y);
+      u[4 * g + 2] = orderable_bits(v.z);
+      u[4 * g + 3] = orderable_bits(v.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * g + e] = base + e < n ? orderable(row[base + e]) : 0u;
+    }
+  }
+}
+
+// Exclusive prefix over the block in thread order of a packed pair of small counts
+// (low 16 bits, high 16 bits; block totals stay below 65536); *total = block sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* slot, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) slot[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kRW; ++w) {
+    const int s = slot[w];
+    before += w < wave ? s : 0;
+    all += s;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Empty asm that "modifies" each register key: keeps the compiler from holding one lane mask
+// per key between the two loops of compact() (64 SGPR pairs at 64 keys per thread) instead of
+// evaluating the predicate again.
+template <int KPT>
+__device__ __forceinline__ void launder(uint32_t (&u)[KPT]) {
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) asm volatile("" : "+v"(u[r]));
+}
+
+// Block-wide compaction in an unspecified order: every item k < ITEMS of the thread for which
+// pred(k) holds is passed to store(pos, k) with distinct pos in [0, total); returns the total.
+// refresh() runs between the counting and the storing loop.
+template <int ITEMS, class Pred, class Store, class Refresh>
+__device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, RegShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) cnt += __popcll(__ballot(pred(k)));
+  if (lane == 0) sh.wcnt[0][wave] = cnt;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRW; ++w) {
+    const int c = sh.wcnt[0][w];
+    base += w < wave ? c : 0;
+    total += c;
+  }
+  refresh();
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const bool p = pred(k);
+    const uint64_t m = __ballot(p);
+    if (p) store(base + lanes_below(m), k);
+    base += __popcll(m);
+  }
+  __syncthreads();
+  return total;
+}
+
+// One wave finds the bin of hist holding the kRem-th largest key (counting from bin 255 down)
+// and the number of keys in bins above it; the block reads them from sh.found after the
+// barrier.
+__device__ __forceinline__ void find_bin(RegShared& sh, int kRem) {
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const int h0 = sh.hist[4 * l], h1 = sh.hist[4 * l + 1], h2 = sh.hist[4 * l + 2],
+              h3 = sh.hist[4 * l + 3];
+    const int s3 = h3, s2 = h2 + s3, s1 = h1 + s2, s0 = h0 + s1;
+    int incl = s0;  // keys in bins >= 4l
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_down(incl, o);
+      if (l + o < 64) incl += t;
+    }
+    const int ex = incl - s0;  // keys in bins >= 4l + 4
+    const int cum[4] = {ex + s0, ex + s1, ex + s2, ex + s3};
+    const int h[4] = {h0, h1, h2, h3};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (cum[q] >= kRem && cum[q] - h[q] < kRem) {
+        sh.found[0] = 4 * l + q;
+        sh.found[1] = cum[q] - h[q];
+      }
+  }
+  __syncthreads();
+}
+
+struct Threshold {
+  uint32_t T;   // the kSel-th largest key
+  int need;     // keys equal to T that are selected (the smallest ids among them)
+  int ties;     // keys equal to T
+  int nc;       // keys in LDS candidates (candU/candId), -1 when the passes ran on registers
+};
+
+// Exact radix select of the kSel-th largest key of the (padded) row held in registers, kSel <= n.
+template <int KPT>
+__device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n, int kSel,
+                                                     RegShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // window [lo, hi]: at least kSel keys are >= lo.  From n = 4 * kRT on, every thread holds
+  // real keys and lo is the smallest thread maximum; below, lo is the smallest real key.
+  uint32_t tmax = 0u;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) tmax = u[r] > tmax ? u[r] : tmax;
+  uint32_t tmin = tmax;
+  if (n < 4 * kRT) {
+    tmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r)
+      if (key_id(r, tid) < n) tmin = u[r] < tmin ? u[r] : tmin;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = __shfl_xor(tmax, o), b = __shfl_xor(tmin, o);
+    tmax = a > tmax ? a : tmax;
+    tmin = b < tmin ? b : tmin;
+  }
+  if (lane == 0) {
+    sh.red[0][wave] = tmax;
+    sh.red[1][wave] = tmin;
+  }
+  __syncthreads();
+  uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kRW; ++w) {
+    hi = sh.red[0][w] > hi ? sh.red[0][w] : hi;
+    lo = sh.red[1][w] < lo ? sh.red[1][w] : lo;
+  }
+  uint32_t wlo = lo, wm1 = hi - lo;  // window [wlo, wlo + wm1]
+  int kRem = kSel, nc = -1;
+  for (int pass = 0; pass < 5; ++pass) {
+    const int bits = wm1 ? 32 - __clz(wm1) : 0;
+    const int shift = bits > 8 ? bits - 8 : 0;
+    __syncthreads();  // readers of the previous pass's hist / found are done
+    for (int j = tid; j < 256; j += kRT) sh.hist[j] = 0;
+    if (tid == 0) {
+      sh.found[0] = 0;
+      sh.found[1] = 0;
+    }
+    __syncthreads();
+    if (nc >= 0) {
+      for (int c = tid; c < nc; c += kRT) {
+        const uint32_t d = sh.candU[c] - wlo;
+        if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const uint32_t d = u[r] - wlo;
+        if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
+      }
+    }
+    __syncthreads();
+    find_bin(sh, kRem);
+    const int bin = sh.found[0] & 255, above = sh.found[1];
+    const int inBin = sh.hist[bin];
+    kRem -= above;
+    const uint32_t off = (uint32_t)bin << shift;
+    wlo += off;
+    const uint32_t binM1 = (1u << shift) - 1u, restM1 = wm1 - off;
+    wm1 = binM1 < restM1 ? binM1 : restM1;
+    if (shift == 0) return Threshold{wlo, kRem, inBin, nc};
+    if (nc < 0 && (kSel - kRem) + inBin <= kCandCap) {
+      // keep the keys >= wlo (those above the new window are selected for certain)
+      const uint32_t T = wlo;
+      nc = compact<KPT>(
+          [&](int r) { return u[r] >= T; },
+          [&](int pos, int r) {
+            if (pos < kCandCap) {
+              sh.candU[pos] = u[r];
+              sh.candId[pos] = key_id(r, tid);
+            }
+          },
+          [&] { launder<KPT>(u); }, sh);
+      if (nc > kCandCap) nc = kCandCap;  // cannot happen: the count is exact
+    }
+  }
+  return Threshold{wlo, kRem, 0, nc};  // not reached: the shift reaches 0 within 4 passes
+}
+
+// The selected keys in ascending id (registers): above T, then the first `need` keys equal to
+// T (padding keys have the largest ids and are never among them).  emit(pos, id, u) receives
+// each selected key with its rank pos in ascending id.
+template <int KPT, class Emit>
+__device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_t T, int need,
+                                               RegShared& sh, Emit emit) {
+  const int tid = threadIdx.x;
+  int aboveRun = 0, tieRun = 0;
+#pragma unroll
+  for (int g = 0; g < KPT / 4; ++g) {
+    bool ab[4], ti[4];
+    int packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      ab[e] = u[r] > T;
+      ti[e] = u[r] == T;
+      packed += (ab[e] ? 1 : 0) + (ti[e] ? 0x10000 : 0);
+    }
+    int tot;
+    const int ex = block_excl_scan(packed, sh.wcnt[g & 1], &tot);
+    int a = aboveRun + (ex & 0xFFFF), t = tieRun + (ex >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      if (ab[e]) {
+        emit(a + (t < need ? t : need), key_id(r, tid), u[r]);
+        ++a;
+      } else if (ti[e]) {
+        if (t < need) emit(a + t, key_id(r, tid), u[r]);
+        ++t;
+      }
+    }
+    aboveRun += tot & 0xFFFF;
+    tieRun += tot >> 16;
+  }
+  __syncthreads();
+}
+
+// Bitonic sort, descending, of kRT * E 64-bit values; thread t holds elements e * kRT + t.
+template <int E>
+__device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf) {
+  const int tid = threadIdx.x;
+  constexpr int P = kRT * E;
+#pragma unroll
+  for (int k = 2; k <= P; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kRT) {
+        const int je = j / kRT;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & je) continue;
+          const bool desc = ((e * kRT + tid) & k) == 0;
+          const uint64_t x = v[e], y = v[e | je];
+          const bool sw = desc ? x < y : x > y;
+          v[e] = sw ? y : x;
+          v[e | je] = sw ? x : y;
+        }
+      } else {
+        if (j >= 64) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) buf[e * kRT + tid] = v[e];
+          __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int x = e * kRT + tid;
+          const uint64_t w = j >= 64 ? buf[x ^ j] : shfl_xor64(v[e], j);
+          const bool keepMax = ((x & k) == 0) == ((x & j) == 0);
+          const bool wBig = w > v[e];
+          v[e] = (keepMax == wBig) ? w : v[e];
+        }
+        if (j >= 64) __syncthreads();
+      }
+    }
+  }
+}
+
+// Sort the m composites of sh.sortBuf[0, m) and leave the ids of the first kSel in sh.selId.
+template <int E>
+__device__ __forceinline__ void sort_selected(int m, int kSel, RegShared& sh) {
+  const int tid = threadIdx.x;
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = e * kRT + tid < m ? sh.sortBuf[e * kRT + tid] : 0ull;
+  __syncthreads();
+  sort_desc<E>(v, sh.sortBuf);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e * kRT + tid < kSel) sh.selId[e * kRT + tid] = (int32_t)~(uint32_t)v[e];
+  __syncthreads();
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kRT) void topk_expand_reg_kernel(TopkArgs a) {
+  __shared__ RegShared sh;
+  const int tid = threadIdx.x;
+  const int64_t i = blockIdx.x, r = a.rowStart + i, b = r / a.S, t = r % a.S;
+  int32_t* out = a.outIdx + r * kIndexWidth;
+  const int64_t c = a.ctx[b];
+  if (c <= 0 || t >= c) {
+    for (int s = tid; s < kIndexWidth; s += kRT) out[s] = -1;
+    return;
+  }
+  const int64_t nVisT = (t + 1) / 4;
+  const int n = (int)(nVisT < a.numBlocks ? nVisT : a.numBlocks);  // <= kRT * KPT (host)
+  const int kSel = n < kTopK ? n : kTopK;
+  const float* row = a.logits + i * a.numBlocks;
+  const bool vec = (a.numBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
+  uint32_t u[KPT];
+  load_keys<KPT>(row, n, vec, u);
+  int m;
+  if (n <= kTopK) {
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int id = key_id(q, tid);
+      if (id < n) sh.sortBuf[id] = composite(u[q], id);
+    }
+    m = n;
+  } else {
+    const Threshold th = select_threshold<KPT>(u, n, kSel, sh);
+    m = (kSel - th.need) + th.ties;
+    if (m <= 2 * kTopK) {
+      const uint32_t T = th.T;
+      if (th.nc >= 0) {
+        const int nc = th.nc;
+        compact<kCandCap / kRT>(
+            [&](int k) {
+              const int q = k * kRT + tid;
+              return q < nc && sh.candU[q] >= T;
+            },
+            [&](int pos, int k) {
+              const int q = k * kRT + tid;
+              if (pos < 2 * kTopK) sh.sortBuf[pos] = composite(sh.candU[q], sh.candId[q]);
+            },
+            [] {}, sh);
+      } else {
+        compact<KPT>([&](int q) { return u[q] >= T; },
+                     [&](int pos, int q) {
+                       if (pos < 2 * kTopK) sh.sortBuf[pos] = composite(u[q], key_id(q, tid));
+                     },
+                     [&] { launder<KPT>(u); }, sh);
+      }
+    } else {
+      ordered_select<KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t uu) {
+        if (pos < kTopK) sh.sortBuf[pos] = composite(uu, id);
+      });
+      m = kSel;
+    }
+  }
+  __syncthreads();
+  if (m <= kTopK) sort_selected<1>(m, kSel, sh);
+  else sort_selected<2>(m, kSel, sh);
+  for (int s = tid; s < 4 * kSel; s += kRT) out[s] = sh.selId[s >> 2] * 4 + (s & 3);
+  write_tail_and_pad(out, 4 * kSel, nVisT, (int)((t + 1) % 4), kRT);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kRT) void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
+  __shared__ RegShared sh;
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  int32_t* out = a.outIdx + b * kIndexWidth;
+  if (a.splitCounters != nullptr)
+    for (int h = tid; h < a.numKVHeads; h += kRT) a.splitCounters[b * a.numKVHeads + h] = 0;
+  const int64_t c = a.ctx[b];
+  if (c <= 0) {
+    for (int s = tid; s < kIndexWidth; s += kRT) out[s] = -1;
+    return;
+  }
+  const int64_t nVisC = c / 4;
+  const int n = (int)(nVisC < a.maxBlocks ? nVisC : a.maxBlocks);  // <= kRT * KPT (host)
+  const int kSel = n < kTopK ? n : kTopK;
+  if (n <= kTopK) {
+    for (int s = tid; s < 4 * n; s += kRT) out[s] = s;  // block s/4, token s%4
+  } else {
+    const float* row = a.logits + b * a.maxBlocks;
+    const bool vec = (a.maxBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
+    uint32_t u[KPT];
+    load_keys<KPT>(row, n, vec, u);
+    const Threshold th = select_threshold<KPT>(u, n, kSel, sh);
+    ordered_select<KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t) {
+      if (pos < kTopK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[4 * pos + j] = 4 * id + j;
+      }
+    });
+  }
+  write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kRT);
+}
+
+// ------------------------------------------------------------------------ streaming ---
 
 // Inclusive suffix sum over the 256 threads of the block: thread j returns sum_{i >= j} v_i.
 __device__ __forceinline__ int block_suffix_sum(int v, int* sh) {
@@ -77,7 +537,8 @@ struct SelectShared {
 };
 
 // The kSel-th largest orderable key T of keys[0, n) and the number of keys equal to T that
-// the selection takes (in ascending id): every key > T is selected.
+// the selection takes (in ascending id): every key > T is selected.  Per pass each wave
+// histograms the digit of the keys that match the prefix found so far into its own bins.
 __device__ void radix_select(const float* keys, int n, int kSel, SelectShared& sh,
                              uint32_t* thr, int* need) {
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -110,40 +571,10 @@ __device__ void radix_select(const float* keys, int n, int kSel, SelectShared& s
   *need = kRem;
 }
 
-__device__ __forceinline__ void write_tail_and_pad(int* out, int from, int64_t nVis, int tail) {
-  for (int s = from + threadIdx.x; s < kIndexWidth; s += kSelThreads)
-    out[s] = s - from < tail ? (int)(4 * nVis + (s - from)) : -1;
-}
-
-// ------------------------------------------------------------------------------ kernels ---
-
-__global__ __launch_bounds__(kSelThreads) void ids_fill_kernel(int32_t* ids, int64_t total,
-                                                               int32_t numBlocks) {
-  for (int64_t i = (int64_t)blockIdx.x * kSelThreads + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * kSelThreads)
-    ids[i] = (int32_t)(i % numBlocks);
-}
-
-// K4: one workgroup per row of the chunk; threads stride the 2051 output slots.
-__global__ __launch_bounds__(kSelThreads) void expand_kernel(ExpandArgs a) {
-  const int64_t i = blockIdx.x, r = a.rowStart + i, b = r / a.S, t = r % a.S;
-  int32_t* out = a.outIdx + r * kIndexWidth;
-  const int64_t c = a.ctx[b];
-  if (c <= 0 || t >= c) {
-    for (int s = threadIdx.x; s < kIndexWidth; s += kSelThreads) out[s] = -1;
-    return;
-  }
-  const int64_t nVis = (t + 1) / 4;
-  const int kSel = (int)(nVis < kTopK ? nVis : kTopK);
-  const int tail = (int)((t + 1) % 4);
-  const int32_t* srt = a.sortedIds + i * a.numBlocks;
-  for (int s = threadIdx.x; s < 4 * kSel; s += kSelThreads) out[s] = srt[s >> 2] * 4 + (s & 3);
-  write_tail_and_pad(out, 4 * kSel, nVis, tail);
-}
-
-// Prefill selection + K4 for one row of the chunk.  Candidates are the row's visible blocks
-// [0, nVis): the entries past them are -FLT_MAX by the scores contract and are not read.
-__global__ __launch_bounds__(kSelThreads) void topk_expand_kernel(TopkArgs a) {
+// Prefill selection + K4 for one row of the chunk (rows longer than the register-resident
+// kernels hold).  Candidates are the row's visible blocks [0, nVis): the entries past them
+// are -FLT_MAX by the scores contract and are not read.
+__global__ __launch_bounds__(kSelThreads) void topk_expand_stream_kernel(TopkArgs a) {
   __shared__ SelectShared sh;
   __shared__ uint32_t selKey[kTopK];
   __shared__ int32_t selId[kTopK];
@@ -207,13 +638,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_expand_kernel(TopkArgs a) {
     }
   }
   for (int s = tid; s < 4 * kSel; s += kSelThreads) out[s] = selId[s >> 2] * 4 + (s & 3);
-  write_tail_and_pad(out, 4 * kSel, nVisT, (int)((t + 1) % 4));
+  write_tail_and_pad(out, 4 * kSel, nVisT, (int)((t + 1) % 4), kSelThreads);
 }
 
-// Decode selection + expand for one sequence: nVis = ctx/4 (capped at maxBlocks); nVis <= 512
-// takes every block without reading logits; the selection is emitted in ascending block id.
-// The sequence's split counters of the attention that follows are zeroed first.
-__global__ __launch_bounds__(kSelThreads) void topk_expand_decode_kernel(TopkDecodeArgs a) {
+// Decode selection + expand for one sequence (rows longer than the register-resident kernels
+// hold): the selection is emitted in ascending block id.  The sequence's split counters of
+// the attention that follows are zeroed first.
+__global__ __launch_bounds__(kSelThreads) void topk_expand_decode_stream_kernel(TopkDecodeArgs a) {
   __shared__ SelectShared sh;
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -252,7 +683,42 @@ __global__ __launch_bounds__(kSelThreads) void topk_expand_decode_kernel(TopkDec
       selBefore += selTot;
     }
   }
-  write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4));
+  write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kSelThreads);
+}
+
+// ------------------------------------------------------------------------------ K4 etc ---
+
+__global__ __launch_bounds__(kSelThreads) void ids_fill_kernel(int32_t* ids, int64_t total,
+                                                               int32_t numBlocks) {
+  for (int64_t i = (int64_t)blockIdx.x * kSelThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kSelThreads)
+    ids[i] = (int32_t)(i % numBlocks);
+}
+
+// K4: one workgroup per row of the chunk; threads stride the 2051 output slots.
+__global__ __launch_bounds__(kSelThreads) void expand_kernel(ExpandArgs a) {
+  const int64_t i = blockIdx.x, r = a.rowStart + i, b = r / a.S, t = r % a.S;
+  int32_t* out = a.outIdx + r * kIndexWidth;
+  const int64_t c = a.ctx[b];
+  if (c <= 0 || t >= c) {
+    for (int s = threadIdx.x; s < kIndexWidth; s += kSelThreads) out[s] = -1;
+    return;
+  }
+  const int64_t nVis = (t + 1) / 4;
+  const int kSel = (int)(nVis < kTopK ? nVis : kTopK);
+  const int tail = (int)((t + 1) % 4);
+  const int32_t* srt = a.sortedIds + i * a.numBlocks;
+  for (int s = threadIdx.x; s < 4 * kSel; s += kSelThreads) out[s] = srt[s >> 2] * 4 + (s & 3);
+  write_tail_and_pad(out, 4 * kSel, nVis, tail, kSelThreads);
+}
+
+// Keys per thread for rows of up to n keys: a multiple of 4 from a short list, or 0 when the
+// row is longer than the register-resident kernels hold.
+int keys_per_thread(int64_t n) {
+  static const int kList[] = {4, 8, 16, 24, 32, 40, 48, 64};
+  for (int k : kList)
+    if (n <= (int64_t)k * kRT) return k;
+  return 0;
 }
 
 }  // namespace
@@ -270,16 +736,45 @@ hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#define QSA_REG_CASES(KERNEL, GRID, ARGS)                                                      \
+  switch (kpt) {                                                                               \
+    case 4: hipLaunchKernelGGL(KERNEL<4>, GRID, dim3(kRT), 0, stream, ARGS); break;            \
+    case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(kRT), 0, stream, ARGS); break;            \
+    case 16: hipLaunchKernelGGL(KERNEL<16>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+    case 24: hipLaunchKernelGGL(KERNEL<24>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+    case 32: hipLaunchKernelGGL(KERNEL<32>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+    case 40: hipLaunchKernelGGL(KERNEL<40>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+    case 48: hipLaunchKernelGGL(KERNEL<48>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+    default: hipLaunchKernelGGL(KERNEL<64>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+  }
+
 hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_expand_kernel, dim3((unsigned)a.numRows), dim3(kSelThreads), 0, stream,
-                     a);
+  // largest number of complete blocks a row of the chunk can have
+  const int64_t r0 = a.rowStart, r1 = a.rowStart + a.numRows - 1;
+  const int64_t tMax = (r0 / a.S == r1 / a.S) ? r1 % a.S : (int64_t)a.S - 1;
+  int64_t nMax = (tMax + 1) / 4;
+  if (nMax > a.numBlocks) nMax = a.numBlocks;
+  const int kpt = keys_per_thread(nMax);
+  const dim3 grid((unsigned)a.numRows);
+  if (kpt == 0) {
+    hipLaunchKernelGGL(topk_expand_stream_kernel, grid, dim3(kSelThreads), 0, stream, a);
+  } else {
+    QSA_REG_CASES(topk_expand_reg_kernel, grid, a)
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_expand_decode_kernel, dim3((unsigned)a.B), dim3(kSelThreads), 0,
-                     stream, a);
+  const int kpt = keys_per_thread(a.maxBlocks);
+  const dim3 grid((unsigned)a.B);
+  if (kpt == 0) {
+    hipLaunchKernelGGL(topk_expand_decode_stream_kernel, grid, dim3(kSelThreads), 0, stream, a);
+  } else {
+    QSA_REG_CASES(topk_expand_decode_reg_kernel, grid, a)
+  }
   return hipGetLastError();
 }
+
+#undef QSA_REG_CASES
 
 }  // namespace qsa

@@ -88,6 +88,82 @@ def test_topk_expand_prefill(qsa, O, case):
     print(f"[parity] topk_expand {case}: {n} rows bit-exact ({sel} indices)", flush=True)
 
 
+# Long rows: name -> (B, S, numBlocks, ctx, rowStart, numRows, styles).  Their outputs span
+# B*S rows, so rows outside the chunk are checked on the device and only the chunk is copied.
+LONG_CASES = {
+    # 64 keys per thread: the long-prefill shape, rows at the end of a 131072-token sequence
+    "full32k": (1, 131072, 32768, [131072], 131072 - 40, 40,
+                ("scores", "normal", "ties", "special_ge", "zeros")),
+    # 20 keys per thread (24 registers), mid-sequence rows
+    "mid": (1, 40000, 10000, [40000], 20000, 64, ("scores", "normal", "ties", "special_ge")),
+    # a chunk across two sequences: short rows of sequence 1 beside long rows of sequence 0
+    "cross": (2, 12000, 3000, [12000, 11000], 11990, 30, ("scores", "normal")),
+    # rows longer than the register-resident kernels hold (streaming kernel)
+    "stream": (1, 140000, 35000, [140000], 140000 - 6, 6, ("scores", "normal", "ties")),
+}
+
+
+def _long_case(case):
+    B, S, nb, ctx, r0, n, styles = LONG_CASES[case]
+    ctx = np.array(ctx, np.int32)
+    styles = tuple("ties" if s == "zeros" else s for s in styles)
+    logits = W.prefill_logits(17, ctx, S, nb, r0, n, styles)
+    if "zeros" in LONG_CASES[case][6]:
+        k = LONG_CASES[case][6].index("zeros")
+        for i in range(k, n, len(LONG_CASES[case][6])):
+            logits[i][logits[i] > -W.FLT_MAX] = 0.0
+    return B, S, nb, ctx, r0, n, logits
+
+
+def _run_long(qsa, O, B, S, nb, ctx, r0, n, logits, what):
+    ref, _ = O.topk_expand(logits, ctx, B, S, r0, n)   # rows outside the chunk stay untouched
+    out = G.Guarded((B * S, WIDTH), torch.int32, fill=POISON)
+    print(f"[gpu] topk_expand {what} B={B} S={S} nb={nb} rows=[{r0},{r0 + n})", flush=True)
+    qsa.qsa_index_topk_expand(out.t, G.dev(logits), G.dev(ctx), B, S, nb, r0, n)
+    torch.cuda.synchronize()
+    out.check()
+    assert bool((out.t[:r0] == POISON).all()) and bool((out.t[r0 + n:] == POISON).all()), \
+        f"{what}: rows outside the chunk written"
+    got = out.t[r0:r0 + n].cpu().numpy()
+    bad = np.flatnonzero(np.any(got != ref[r0:r0 + n], axis=1))
+    assert bad.size == 0, f"{what}: {bad.size} rows differ, first global row {r0 + bad[0]}"
+    print(f"[parity] topk_expand {what}: {n} rows bit-exact", flush=True)
+
+
+@pytest.mark.parametrize("case", list(LONG_CASES))
+def test_topk_expand_long_rows(qsa, O, case):
+    """Rows of 3000 to 35000 complete blocks: every register width of the register-resident
+    kernel up to 64 keys per thread, a chunk across two sequences, and the streaming kernel past
+    32768 blocks; value styles with recurring values, many ties at the threshold (all equal
+    included), +-0, +-inf, NaN and -FLT_MAX."""
+    _run_long(qsa, O, *_long_case(case), case)
+
+
+def test_topk_expand_all_ones_nan(qsa, O):
+    """Keys at the bottom of the order (FP32 bits 0xFFFFFFFF map to 0): a row made only of
+    them (the threshold is 0 and padding keys equal it), a row where one thread's keys are all
+    such NaNs (the radix window then starts at 0), and a row that is mostly NaN with 600
+    ordinary values.  numBlocks < nVis, so every entry is a complete block."""
+    B, S, nb = 1, 12100, 3000
+    ctx = np.array([S], np.int32)
+    r0, n = S - 9, 9
+    rng = np.random.default_rng(23)
+    logits = rng.standard_normal((n, nb)).astype(np.float32)
+    bits = logits.view(np.uint32)
+    bits[0::3] = 0xFFFFFFFF
+    bits[1::3, 1200:1204] = 0xFFFFFFFF
+    for i in range(2, n, 3):
+        keep = rng.choice(nb, 600, replace=False)
+        row = np.full(nb, 0xFFFFFFFF, np.uint32)
+        row[keep] = bits[i, keep]
+        bits[i] = row
+    _run_long(qsa, O, B, S, nb, ctx, r0, n, logits, "all-ones NaN")
+    # the same with a row of 700 blocks (a single register group, row-minimum window)
+    nb2 = 700
+    lg2 = np.ascontiguousarray(logits[:, :nb2])
+    _run_long(qsa, O, B, S, nb2, ctx, r0, n, lg2, "all-ones NaN, 700 blocks")
+
+
 @pytest.mark.parametrize("case", ["ragged", "chunk"])
 def test_expand_prefill(qsa, O, case):
     """K4 alone, fed with the oracle's sorted ids (the page's sort output)."""
@@ -105,7 +181,7 @@ def test_expand_prefill(qsa, O, case):
     assert np.array_equal(ref2, ref)
 
 
-@pytest.mark.parametrize("maxBlocks", [4096, 512, 600])
+@pytest.mark.parametrize("maxBlocks", [4096, 512, 600, 2000, 32768, 40000])
 def test_topk_expand_decode(qsa, O, maxBlocks):
     """64 sequences: ctx <= 0, ctx/4 below, at and above 512, above 4*maxBlocks (capped), all
     four logit styles including -inf and NaNs of both signs."""
@@ -125,3 +201,30 @@ def test_topk_expand_decode(qsa, O, maxBlocks):
     bad = np.flatnonzero(np.any(got != ref, axis=1))
     assert bad.size == 0, f"{bad.size} sequences differ, first {bad[0]} (ctx {ctx[bad[0]]})"
     print(f"[parity] topk_expand_decode maxBlocks={maxBlocks}: 64 rows bit-exact", flush=True)
+
+
+def test_topk_expand_decode_all_ones_nan(qsa, O):
+    """Decode rows holding FP32 bits 0xFFFFFFFF (the smallest key): all of them (threshold 0,
+    padding keys equal to it), one register group of them inside ordinary values, and a few
+    hundred ordinary values among them; rows of 700, 3000 and 9000 blocks."""
+    rng = np.random.default_rng(29)
+    maxBlocks = 9000
+    ctx = np.array([4 * 700 + 1, 4 * 3000 + 2, 4 * 9000 + 3] * 3, np.int32)
+    B = len(ctx)
+    logits = rng.standard_normal((B, maxBlocks)).astype(np.float32)
+    bits = logits.view(np.uint32)
+    bits[0:3] = 0xFFFFFFFF
+    bits[3:6, 1200:1204] = 0xFFFFFFFF
+    for b in range(6, 9):
+        keep = rng.choice(min(int(ctx[b]) // 4, maxBlocks), 600, replace=False)
+        row = np.full(maxBlocks, 0xFFFFFFFF, np.uint32)
+        row[keep] = bits[b, keep]
+        bits[b] = row
+    ref = O.topk_expand_decode(logits, ctx)
+    out = G.Guarded((B, WIDTH), torch.int32, fill=POISON)
+    print("[gpu] topk_expand_decode all-ones NaN", flush=True)
+    qsa.qsa_index_topk_expand_decode(out.t, G.dev(logits), G.dev(ctx), maxBlocks)
+    got = _host(out)
+    bad = np.flatnonzero(np.any(got != ref, axis=1))
+    assert bad.size == 0, f"{bad.size} sequences differ, first {bad[0]} (ctx {ctx[bad[0]]})"
+    print(f"[parity] topk_expand_decode all-ones NaN: {B} rows bit-exact", flush=True)
