@@ -55,8 +55,9 @@ int check_eps(float eps) {
 }
 
 // Every kernel runs 256-thread workgroups; a launch's x extent counts work-items in 32 bits.
-int check_grid(int64_t workgroups) {
-  if (workgroups > (int64_t)(UINT32_MAX / 256u))
+// A launch holds at most UINT32_MAX threads; `threads` is the workgroup size.
+int check_grid(int64_t workgroups, int64_t threads = 256) {
+  if (workgroups > (int64_t)UINT32_MAX / threads)
     return fail(QSA_E_INVALID, "problem needs %lld workgroups, more than one launch can hold",
                 (long long)workgroups);
   return QSA_OK;
@@ -336,9 +337,8 @@ QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* 
     return fail(QSA_E_INVALID, "rowStart + numRows = %lld > batchSize * seqLen = %lld",
                 (long long)rowStart + numRows, (long long)rows);
   if (numRows == 0 || numBlocks == 0) return ok();
-  if ((numBlocks + 2047) / 2048 > 65535)
-    return fail(QSA_E_INVALID, "numBlocks = %d exceeds the supported %d", numBlocks,
-                65535 * 2048);
+  if (numBlocks > (1 << 26))  // the kernel addresses 8 logits rows with 32-bit byte offsets
+    return fail(QSA_E_INVALID, "numBlocks = %d exceeds the supported %d", numBlocks, 1 << 26);
   TRY(need(logits, "logits", 4));
   TRY(need(qNormed, "qNormed", 16));
   TRY(need(kbar, "kbar", 16));
@@ -357,7 +357,7 @@ QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* 
   const int64_t last = (int64_t)rowStart + numRows - 1;
   a.tile0 = (rowStart / seqLen) * a.tilesPerSeq + (rowStart % seqLen) / 32;
   a.numTiles = (last / seqLen) * a.tilesPerSeq + (last % seqLen) / 32 - a.tile0 + 1;
-  TRY(check_grid(a.numTiles));
+  TRY(check_grid(a.numTiles * ceil_div(numBlocks, 4096)));
   (void)hipGetLastError();
   return launched(qsa::launch_scores(a, t, static_cast<hipStream_t>(stream)), "qsa_index_scores");
 }
@@ -439,7 +439,7 @@ QSA_EXPORT int qsa_index_topk_expand(int32_t* outIdx, const float* logits,
   TRY(need(outIdx, "outIdx", 4));
   if (numBlocks > 0) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(numRows));
+  TRY(check_grid(numRows, 512));
   const qsa::TopkArgs a{outIdx, logits, contextLengths, seqLen, numBlocks, rowStart, numRows};
   (void)hipGetLastError();
   return launched(qsa::launch_topk_expand(a, static_cast<hipStream_t>(stream)),
@@ -460,7 +460,7 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
   if (splitCounters != nullptr) TRY(need(splitCounters, "splitCounters", 4));
   if (maxBlocks > QSA_TOPK) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(batchSize));
+  TRY(check_grid(batchSize, 512));
   const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
                               splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
   (void)hipGetLastError();

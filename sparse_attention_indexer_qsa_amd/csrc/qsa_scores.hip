@@ -11,17 +11,20 @@
 //  * A operand: 32 rows = 8 consecutive tokens x 4 heads of one sequence.  qNormed is
 //    [B, S, 4, 128], so these 32 head vectors are contiguous and row i = 4*token + head.
 //  * B operand: 32 consecutive kbar rows (blocks).  A workgroup (4 waves, 8 tokens each) keeps
-//    its q fragments in registers and walks 2048 blocks, 128 at a time staged in LDS and
-//    shared by the 4 waves; each wave runs the 4 column tiles of a chunk on 4 independent
-//    accumulators, so consecutive MFMAs do not wait on each other.
+//    its q fragments in registers and walks 4096 blocks, 64 at a time staged in LDS
+//    (double-buffered) and shared by the 4 waves; each wave runs the 2 column tiles of a chunk
+//    on 2 independent accumulators.  64-block chunks keep the LDS at 35 KB and the registers
+//    near 128 per lane, so four workgroups share a CU and hide each other's latency.
 //  * K = 128 in 8 steps of 16.  Every lane loads A and B with the same lane -> k mapping, so
 //    the dot products do not depend on how the instruction orders k.
 //  * In the 32x32 accumulator a lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32
 //    for its 16 registers v: registers 4m..4m+3 are the four heads of token 2m + lane/32.  ReLU,
-//    the ascending head sum and the scale are in-lane, and lanes 0..31 store 32 consecutive
-//    logits of a token (128 bytes).
-//  * Column tiles that no token of the workgroup can see skip the contraction and store
-//    -FLT_MAX.  The kernel is bound by the FP32 logits it writes.
+//    the ascending head sum and the scale are in-lane; lanes 0..31 then store 32 consecutive
+//    logits of one token (a 128-byte line) and lanes 32..63 those of the next token.
+//  * Chunks that every token of the wave sees in full take a path without masks; the chunk
+//    holding a token's visibility edge masks per entry.  Column tiles that no token of the
+//    workgroup can see skip the contraction and store -FLT_MAX.  The kernel is bound by the
+//    FP32 logits it writes.
 //
 // Decode gathers kbar rows from the paged pool (one 16-lane DPP row per block, the 4+4 dims
 // split of qsa_device.h), four FP32 dot products per block reduced by DPP, on the VALU.
@@ -40,9 +43,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kSTokWave = 8;                       // tokens per wave
 constexpr int kSTokWG = kSTokWave * kWaves;        // tokens per workgroup (32)
 constexpr int kSColTile = 32;                      // blocks per MFMA column tile
-constexpr int kSColTiles = 4;                      // column tiles per staged chunk
-constexpr int kSChunk = kSColTile * kSColTiles;    // blocks staged in LDS at a time (128)
-constexpr int kSRange = 2048;                      // blocks walked by one workgroup
+constexpr int kSColTiles = 2;                      // column tiles per staged chunk
+constexpr int kSChunk = kSColTile * kSColTiles;    // blocks staged in LDS at a time (64)
+constexpr int kSPieces = kSChunk * 16 / kThreads;  // 16-byte kbar pieces staged per thread
+constexpr int kSRange = 4096;                      // blocks walked by one workgroup
 
 __device__ __forceinline__ float score_scale() { return 1.0f / __builtin_sqrtf(128.0f); }
 
@@ -56,107 +60,125 @@ __device__ __forceinline__ f32x16 mfma32(F16, const uint4& a, const uint4& b, co
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// 4x4 transpose within each DPP quad: on return, lane e of a quad holds in x[m] what lane m
-// held in x[e].  Two butterfly stages (partner lane xor 1, then xor 2), each exchanging the
-// registers whose index differs from the lane's in that bit.
-__device__ __forceinline__ void quad_transpose(float (&x)[4], int e) {
-  float y[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float t = dpp_f<0xB1>(x[m ^ 1]);  // quad_perm [1,0,3,2]: lane e ^ 1
-    y[m] = ((e ^ m) & 1) ? t : x[m];
-  }
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float t = dpp_f<0x4E>(y[m ^ 2]);  // quad_perm [2,3,0,1]: lane e ^ 2
-    x[m] = ((e ^ m) & 2) ? t : y[m];
-  }
+// Sum over the four heads, ascending, of relu(d_h) = d_h > 0 ? d_h : +0 (so -0 and NaN give
+// +0), as ((relu(d0) + relu(d1)) + relu(d2)) + relu(d3).  For p >= +0, p + relu(d) has the
+// same bits as max(p + d, p) (d <= 0, -0, NaN or -inf leave p; otherwise the rounded p + d is
+// >= p), and both operands of that max are results of IEEE operations, so the compiler needs
+// no canonicalising instruction before it: 2 instructions per head after the first.
+__device__ __forceinline__ float relu_head_sum(float d0, float d1, float d2, float d3) {
+  float p = d0 > 0.0f ? d0 : 0.0f;
+  p = __builtin_fmaxf(p + d1, p);
+  p = __builtin_fmaxf(p + d2, p);
+  return __builtin_fmaxf(p + d3, p);
 }
 
-// Global rows [rowLo, rowHi) of the logits chunk.  Workgroup tile `tile0 + blockIdx.x` is
-// tokens [32*(tile % tilesPerSeq), +32) of sequence tile / tilesPerSeq; blockIdx.y picks a
-// range of 2048 blocks, walked in chunks of 128 staged in LDS (double-buffered: the next
-// chunk's loads are in flight while the current one is contracted).  The q fragments of the
-// workgroup's tokens stay in registers for the whole range.
+// Global rows [rowLo, rowHi) of the logits chunk.  Workgroup tile `tile` is tokens
+// [32*(tile % tilesPerSeq), +32) of sequence tile / tilesPerSeq, over one range of 4096
+// blocks, walked in chunks of 64 staged in LDS (double-buffered: the next chunk's loads are in
+// flight while the current one is contracted).  The q fragments of the workgroup's tokens stay
+// in registers for the whole range.
 template <class T>
-__global__ __launch_bounds__(kThreads) void scores_kernel(ScoresArgs a) {
-  // 2 x 128 kbar rows x 256 bytes, rows padded to 272 bytes so that 32 lanes reading one
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void scores_kernel(ScoresArgs a) {
+  // 2 x 64 kbar rows x 256 bytes, rows padded to 272 bytes so that 32 lanes reading one
   // 16-byte piece of 32 different rows spread over the LDS banks
   __shared__ uint4 kb_lds[2][kSChunk][17];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t tile = a.tile0 + blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
+  // workgroup w takes tile tile0 + w % numTiles over range w / numTiles: the workgroups in
+  // flight together read the same few kbar ranges, which stay in cache
+  const int64_t tile = a.tile0 + blockIdx.x % a.numTiles;
+  const int rangeIdx = (int)(blockIdx.x / a.numTiles);
   const int64_t b = tile / a.tilesPerSeq;
-  const int64_t t0 = (tile % a.tilesPerSeq) * kSTokWG;
-  const int64_t S = a.S, nB = a.numBlocks;
-  const int64_t rangeLo = (int64_t)blockIdx.y * kSRange;
-  const int64_t rangeHi = rangeLo + kSRange < nB ? rangeLo + kSRange : nB;
+  const int t0 = (int)(tile % a.tilesPerSeq) * kSTokWG;
+  const int S = a.S, nB = a.numBlocks;
+  const int rangeLo = rangeIdx * kSRange;
+  const int rangeHi = rangeLo + kSRange < nB ? rangeLo + kSRange : nB;
   const int64_t rowLo = a.rowStart, rowHi = a.rowStart + a.numRows;
-  const int64_t ctx = a.ctx[b];
+  const int64_t seqRow0 = b * S;                    // global row of token 0 of the sequence
+  const int ctx = a.ctx[b];
+  // token range [tLo, tHi) of the sequence whose rows are in the chunk
+  const int tLo = rowLo > seqRow0 ? (int)(rowLo - seqRow0) : 0;
+  const int tHi = rowHi - seqRow0 < S ? (int)(rowHi - seqRow0) : S;
   // last token of the workgroup that is a real, unpadded row of the chunk
-  int64_t tLast = t0 + kSTokWG - 1;
-  if (tLast > S - 1) tLast = S - 1;
+  int tLast = t0 + kSTokWG - 1;
+  if (tLast > tHi - 1) tLast = tHi - 1;
   if (tLast > ctx - 1) tLast = ctx - 1;
-  if (tLast > rowHi - 1 - b * S) tLast = rowHi - 1 - b * S;
-  const int64_t nVisWG = tLast >= t0 ? (tLast + 1) / 4 : 0;  // blocks any row here can see
-  const int64_t computeHi = nVisWG < rangeHi ? nVisWG : rangeHi;  // contraction needed below
+  const int nVisWG = tLast >= t0 ? (tLast + 1) / 4 : 0;  // blocks any row here can see
+  const int computeHi = nVisWG < rangeHi ? nVisWG : rangeHi;  // contraction needed below
   const float scale = score_scale();
 
   // A fragments: row i = lane % 32 -> token tw0 + i/4, head i % 4; k-group lane / 32
-  const int64_t tw0 = t0 + kSTokWave * wave;
+  const int tw0 = t0 + kSTokWave * wave;
   const int i = lane & 31, kg = lane >> 5;
-  const int64_t tokA = tw0 + (i >> 2);
-  const bool readA = tokA < S && tokA < ctx && b * S + tokA >= rowLo && b * S + tokA < rowHi &&
-                     rangeLo < computeHi;
+  const int tokA = tw0 + (i >> 2);
+  const bool readA = tokA >= tLo && tokA < tHi && tokA < ctx && rangeLo < computeHi;
   uint4 qa[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
-    qa[ks] = readA ? load16_u4(a.qNormed, ((b * S + tokA) * 4 + (i & 3)) * kDim + 16 * ks + 8 * kg)
+    qa[ks] = readA ? load16_u4(a.qNormed,
+                               ((seqRow0 + tokA) * 4 + (i & 3)) * kDim + 16 * ks + 8 * kg)
                    : make_uint4(0, 0, 0, 0);
 
-  // Output mapping after the quad transpose: lane (i = 4p + e, kg) stores blocks
-  // [4p, 4p+4) of the column tile for token tw0 + 2e + kg (16 bytes).
-  const int e = i & 3, p4 = (i >> 2) * 4;
-  const int64_t tOut = tw0 + 2 * e + kg;
-  const int64_t rOut = b * S + tOut;
-  const bool live = tOut < S && rOut >= rowLo && rOut < rowHi;
-  const int64_t nVisOut = tOut < ctx ? (tOut + 1) / 4 : 0;
-  float* outRow = a.logits + (rOut - rowLo) * nB;
-  // 16-byte stores need every row start 16-byte aligned
-  const bool vec = (nB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
-
-  // staging: 128 rows x 16 pieces per chunk, 8 per thread; rows that no token of the
-  // workgroup can see, or past the range, are zeros and are not read
-  auto fetch = [&](int64_t c0, uint4 (&v)[8]) {
+  // Output: lane (i, kg) stores block i of each column tile for tokens tw0 + 2m + kg, m < 4,
+  // at byte offset boff[m] from the wave's first row (uniform base; the host bounds numBlocks
+  // so that 8 rows of offsets fit 32 bits)
+  char* waveRow = reinterpret_cast<char*>(a.logits + (seqRow0 + tw0 - rowLo) * (int64_t)nB);
+  uint32_t boff[4];
+  bool live[4];
+  int nVisOut[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int idx = tid + kThreads * k, row = idx >> 4, piece = idx & 15;
-      const int64_t g = c0 + row;
-      v[k] = g < computeHi ? load16_u4(a.kbar, (b * nB + g) * kDim + 8 * piece)
-                           : make_uint4(0, 0, 0, 0);
-    }
+  for (int m = 0; m < 4; ++m) {
+    const int tok = tw0 + 2 * m + kg;
+    live[m] = tok >= tLo && tok < tHi;
+    nVisOut[m] = tok < ctx ? (tok + 1) / 4 : 0;
+    boff[m] = ((uint32_t)(2 * m + kg) * (uint32_t)nB + (uint32_t)i) * 4u;
+  }
+  // chunks below fastHi are seen in full by all 8 tokens of the wave, all of them live
+  const bool waveLive = tw0 >= tLo && tw0 + kSTokWave <= tHi && tw0 + kSTokWave <= ctx;
+  const int fastHi = waveLive ? ((tw0 + 1) / 4 < rangeHi ? (tw0 + 1) / 4 : rangeHi) : 0;
+
+  // staging: 64 rows x 16 pieces per chunk, 4 per thread.  Rows that no token of the
+  // workgroup can see, or past the range, repeat the last row the workgroup can see (fetch
+  // runs only when that row exists): the logits they feed are all masked (-FLT_MAX) or not
+  // stored.  Straight-line loads with no zero fill keep the compiler from waiting on them
+  // before they are needed.
+  const uint16_t* kbSeq = static_cast<const uint16_t*>(a.kbar) + b * nB * (int64_t)kDim;
+  static_assert(kSPieces == 4, "staging holds 4 pieces per thread");
+  const int srow = tid >> 4, spiece = 8 * (tid & 15);  // pieces: rows srow + 16k, k < 4
+  uint4 v0, v1, v2, v3;
+  auto fetch = [&](int c0) {
+    const int last = computeHi - 1;
+    const int g0 = min(c0 + srow, last), g1 = min(c0 + srow + 16, last);
+    const int g2 = min(c0 + srow + 32, last), g3 = min(c0 + srow + 48, last);
+    v0 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g0 * kDim + spiece);
+    v1 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g1 * kDim + spiece);
+    v2 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g2 * kDim + spiece);
+    v3 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g3 * kDim + spiece);
   };
-  auto stash = [&](int buf, const uint4 (&v)[8]) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int idx = tid + kThreads * k;
-      kb_lds[buf][idx >> 4][idx & 15] = v[k];
-    }
+  auto stash = [&](int buf) {
+    kb_lds[buf][srow][tid & 15] = v0;
+    kb_lds[buf][srow + 16][tid & 15] = v1;
+    kb_lds[buf][srow + 32][tid & 15] = v2;
+    kb_lds[buf][srow + 48][tid & 15] = v3;
   };
 
-  uint4 v[8];
   if (rangeLo < computeHi) {
-    fetch(rangeLo, v);
-    stash(0, v);
+    fetch(rangeLo);
+    stash(0);
   }
   // chunks at or past fillLo hold nothing any row of the workgroup can see: they are written
   // as -FLT_MAX row by row after the contraction loop
-  const int64_t fillLo = rangeLo + (computeHi > rangeLo ? (computeHi - rangeLo + kSChunk - 1) /
-                                                               kSChunk * kSChunk : 0);
+  const int fillLo = rangeLo + (computeHi > rangeLo ? (computeHi - rangeLo + kSChunk - 1) /
+                                                          kSChunk * kSChunk : 0);
+  // no global load may be outstanding on entry: a wait for the q fragments inside the loop
+  // would also wait for the next chunk's prefetch (vmcnt(0); expcnt and lgkmcnt unchanged)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   int buf = 0;
-  for (int64_t c0 = rangeLo; c0 < fillLo; c0 += kSChunk) {
+  for (int c0 = rangeLo; c0 < fillLo; c0 += kSChunk) {
     __syncthreads();  // chunk c0 is in kb_lds[buf]; every wave is done with the other buffer
     const bool more = c0 + kSChunk < computeHi;
-    if (more) fetch(c0 + kSChunk, v);  // in flight during the contraction
+    if (more) fetch(c0 + kSChunk);  // in flight during the contraction
     f32x16 acc[kSColTiles];
 #pragma unroll
     for (int ct = 0; ct < kSColTiles; ++ct) acc[ct] = f32x16{};
@@ -166,43 +188,46 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoresArgs a) {
       for (int ct = 0; ct < kSColTiles; ++ct)
         acc[ct] = mfma32(T{}, qa[ks], kb_lds[buf][kSColTile * ct + i][2 * ks + kg], acc[ct]);
     // epilogue: registers 4m..4m+3 hold the four heads of token 2m + kg for block i of the
-    // column tile; ReLU per head, ascending head sum, scale, then the quad transpose
+    // column tile; ReLU per head, ascending head sum, scale
+    float x[kSColTiles][4];
 #pragma unroll
-    for (int ct = 0; ct < kSColTiles; ++ct) {
-      float x[4];
+    for (int ct = 0; ct < kSColTiles; ++ct)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        float s = __builtin_fmaxf(acc[ct][4 * m], 0.0f);
-        s = s + __builtin_fmaxf(acc[ct][4 * m + 1], 0.0f);
-        s = s + __builtin_fmaxf(acc[ct][4 * m + 2], 0.0f);
-        s = s + __builtin_fmaxf(acc[ct][4 * m + 3], 0.0f);
-        x[m] = scale * s;
+        x[ct][m] = scale * relu_head_sum(acc[ct][4 * m], acc[ct][4 * m + 1], acc[ct][4 * m + 2],
+                                         acc[ct][4 * m + 3]);
       }
-      quad_transpose(x, e);  // x[k]: token tOut, block p4 + k of the tile
-      const int64_t g = c0 + kSColTile * ct + p4;
-      if (!live || g >= rangeHi) continue;
+    char* chunkRow = waveRow + 4 * (int64_t)c0;
+    if (c0 + kSChunk <= fastHi) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (g + k >= nVisOut) x[k] = -FLT_MAX;
-      if (vec && g + 4 <= rangeHi) {
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]},
-                                    reinterpret_cast<f32x4*>(outRow + g));
-      } else {
-        for (int k = 0; k < 4; ++k)
-          if (g + k < rangeHi) outRow[g + k] = x[k];
+      for (int ct = 0; ct < kSColTiles; ++ct)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          __builtin_nontemporal_store(
+              x[ct][m], reinterpret_cast<float*>(chunkRow + boff[m] + 4 * kSColTile * ct));
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < kSColTiles; ++ct) {
+        const int g = c0 + kSColTile * ct + i;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (live[m] && g < rangeHi)
+            __builtin_nontemporal_store(
+                g < nVisOut[m] ? x[ct][m] : -FLT_MAX,
+                reinterpret_cast<float*>(chunkRow + boff[m] + 4 * kSColTile * ct));
       }
     }
-    if (more) stash(buf ^ 1, v);
+    if (more) stash(buf ^ 1);
     buf ^= 1;
   }
   // -FLT_MAX over [fillLo, rangeHi) of each of the wave's 8 token rows, each row written in
   // contiguous 1 KB runs (64 lanes x 16 bytes)
+  const bool vec = (nB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   for (int k = 0; k < kSTokWave; ++k) {
-    const int64_t t = tw0 + k, r = b * S + t;
-    if (t >= S || r < rowLo || r >= rowHi) continue;
-    float* row = a.logits + (r - rowLo) * nB;
-    for (int64_t g = fillLo + 4 * lane; g < rangeHi; g += 4 * 64) {
+    const int t = tw0 + k;
+    if (t < tLo || t >= tHi) continue;
+    float* row = a.logits + (seqRow0 + t - rowLo) * (int64_t)nB;
+    for (int g = fillLo + 4 * lane; g < rangeHi; g += 4 * 64) {
       if (vec && g + 4 <= rangeHi) {
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         __builtin_nontemporal_store(f32x4{-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX},
@@ -267,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
 }  // namespace
 
 hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream) {
-  const dim3 grid((unsigned)a.numTiles, (unsigned)((a.numBlocks + kSRange - 1) / kSRange));
+  const dim3 grid((unsigned)(a.numTiles * ((a.numBlocks + kSRange - 1) / kSRange)));
   if (dt == Dt::BF16) hipLaunchKernelGGL((scores_kernel<Bf16>), grid, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((scores_kernel<F16>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
