@@ -439,7 +439,7 @@ QSA_EXPORT int qsa_index_topk_expand(int32_t* outIdx, const float* logits,
   TRY(need(outIdx, "outIdx", 4));
   if (numBlocks > 0) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(numRows, 512));
+  TRY(check_grid(numRows));
   const qsa::TopkArgs a{outIdx, logits, contextLengths, seqLen, numBlocks, rowStart, numRows};
   (void)hipGetLastError();
   return launched(qsa::launch_topk_expand(a, static_cast<hipStream_t>(stream)),
@@ -460,7 +460,7 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
   if (splitCounters != nullptr) TRY(need(splitCounters, "splitCounters", 4));
   if (maxBlocks > QSA_TOPK) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(batchSize, 512));
+  TRY(check_grid(batchSize));
   const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
                               splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
   (void)hipGetLastError();

@@ -9,27 +9,29 @@
 // Keys are the monotone map of the FP32 bits, u = bits >= 0 ? bits | 0x80000000 : ~bits; a
 // row's order is descending u, equal u in ascending block id (the stable sort's order).
 //
-// Register-resident rows (up to 64 keys per thread x 512 threads = 32768 blocks):
+// Register-resident rows (up to 128 keys per thread x 256 threads = 32768 blocks):
 //  * The row is read from HBM once, 16 bytes per lane, into registers.  Thread t holds the
-//    ids ((g * 512 + t) * 4 + e) for its register groups g and e < 4.
+//    ids ((g * 256 + t) * 4 + e) for its register groups g and e < 4.
 //  * Padding: registers past the row hold u = 0 with ids >= n.  In the (u desc, id asc)
 //    order every padding key comes after every real key, so while kSel <= n the kSel first
 //    keys of the padded row are those of the row, and no step needs to tell them apart.
-//  * Window: once n >= 2048 every thread holds real keys, and the smallest of the 512
-//    per-thread maxima, lo, has at least 512 keys at or above it (shorter rows take lo = the
-//    row minimum); with hi the row maximum, the kSel-th largest key lies in [lo, hi].
+//  * Window: once n >= 2048 the even and the odd register groups of every thread hold real
+//    keys, and the smallest of those 512 maxima, lo, has at least 512 keys at or above it
+//    (shorter rows take lo = the row minimum); with hi the row maximum, the kSel-th largest
+//    key lies in [lo, hi].
 //  * Radix select inside the window, MSB first: each pass histograms (LDS atomics, 256 bins)
 //    only the keys inside the current window, at a shift that spreads the window over the 256
 //    bins, and a one-wave suffix scan picks the bin holding the kSel-th largest.  The window
-//    keeps only the top few percent of a row, so the bins are spread and the atomics rarely
-//    collide.  After the first pass the keys at or above the chosen bin (a few hundred) are
+//    holds a few thousand keys of a row (about 512 ln 512 for independent keys), so the bins
+//    are spread and the atomics rarely collide.  After the first pass the keys at or above the chosen bin (a few hundred) are
 //    compacted into LDS and the later passes run on them alone.  The result is the threshold
 //    key T, the number `need` of keys equal to T that are taken (ascending id) and their
 //    count `ties`.
 //  * Prefill: the keys >= T (kSel - need + ties of them; ties normally = need) are gathered as
 //    64-bit (u, ~id) composites and sorted descending by a bitonic network (strides < 64 by
-//    lane shuffles, 64..256 through LDS), so equal keys come out in ascending id and the first
-//    kSel are the result.  More than 1024 such keys (many equal keys at T) take the ordered
+//    lane shuffles, 64 and 128 through LDS, larger ones within a thread), so equal keys come
+//    out in ascending id and the first kSel are the result.  More than 1024 such keys (many
+//    equal keys at T), or candidates too many for LDS after the first pass, take the ordered
 //    path below, then the same sort.
 //  * Decode: the selection is emitted in ascending id: one block scan per register group
 //    counts, for each key, the keys above T and the keys equal to T with smaller ids.
@@ -48,7 +50,7 @@ namespace {
 constexpr int kTopK = 512;
 constexpr int kIndexWidth = 2051;   // 4 * 512 + 3
 constexpr int kSelThreads = 256;    // streaming kernels
-constexpr int kRT = 512;            // register-resident kernels: threads per row
+constexpr int kRT = 256;            // register-resident kernels: threads per row
 constexpr int kRW = kRT / 64;       // waves per row
 constexpr int kCandCap = 2048;      // keys kept in LDS after the first radix pass
 
@@ -84,6 +86,15 @@ struct RegShared {
 
 __device__ __forceinline__ int key_id(int r, int tid) { return (((r >> 2) * kRT + tid) << 2) + (r & 3); }
 
+// threadIdx.x through an empty asm: per-key ids derived from it in one branch are not merged
+// with (and hoisted above the radix select as) those of another branch, which would hold a
+// register per key across it.
+__device__ __forceinline__ int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ uint64_t composite(uint32_t u, int id) {
   return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
 }
@@ -98,23 +109,40 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-template <int KPT>
-__device__ __forceinline__ void load_keys(const float* row, int n, bool vec, uint32_t (&u)[KPT]) {
+// The row's keys into registers (padding u = 0), every load issued before any is waited for.
+// kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
+// before n ends inside the row and is one 16-byte load (groups wholly past n load the row's
+// first keys).  Otherwise one load per key at min(id, n - 1).  Keys past n are masked to 0.
+template <int KPT, bool kVec>
+__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)[KPT]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int g = 0; g < KPT / 4; ++g) {
     const int base = (g * kRT + tid) * 4;
-    if (vec && base + 4 <= n) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + base));
-      u[4 * g + 0] = orderable_bits(v.x);
-      u[4 * g + 1] = orderable_bits(v.y);
-      u[4 * g + 2] = orderable_bits(v.z);
-      u[4 * g + 3] = orderable_bits(v.w);
+    const int lim = n - base;  // keys of this group inside the row (<= 0: none)
+    if constexpr (kVec) {
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(row + (lim > 0 ? base : 0)));
+      u[4 * g + 0] = lim > 0 ? orderable_bits(v.x) : 0u;
+      u[4 * g + 1] = lim > 1 ? orderable_bits(v.y) : 0u;
+      u[4 * g + 2] = lim > 2 ? orderable_bits(v.z) : 0u;
+      u[4 * g + 3] = lim > 3 ? orderable_bits(v.w) : 0u;
     } else {
+      const unsigned* r32 = reinterpret_cast<const unsigned*>(row);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[4 * g + e] = base + e < n ? orderable(row[base + e]) : 0u;
+      for (int e = 0; e < 4; ++e) {
+        const unsigned x = __builtin_nontemporal_load(r32 + min(base + e, n - 1));
+        u[4 * g + e] = lim > e ? orderable_bits(x) : 0u;
+      }
     }
   }
+}
+
+// Keeps the scheduler from interleaving the work of more than 8 register keys at a time: the
+// keys already fill most of the register file, and a long interleave holds a temporary per key.
+// (Called from fully unrolled loops, where r is a constant.)
+__device__ __forceinline__ void key_fence(int r) {
+  if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Exclusive prefix over the block in thread order of a packed pair of small counts
@@ -207,6 +235,56 @@ __device__ __forceinline__ void find_bin(RegShared& sh, int kRem) {
   __syncthreads();
 }
 
+// Radix window [wlo, wlo + wm1] holding the kRem-th largest of the keys it covers.
+struct RadixWindow {
+  uint32_t wlo, wm1;
+  int kRem;
+  int inBin;  // after a pass: keys in the chosen bin
+  int shift;  // after a pass: the shift it used (0: the window is now a single key value)
+};
+
+// One radix pass: histogram of the window's keys (registers, or the nc LDS candidates) over
+// 256 bins at a shift that spreads the window over them, then narrow the window to the bin
+// holding the kRem-th largest.
+template <int KPT, bool kLds>
+__device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, RadixWindow& w,
+                                           RegShared& sh) {
+  const int tid = threadIdx.x;
+  const int bits = w.wm1 ? 32 - __clz(w.wm1) : 0;
+  const int shift = bits > 8 ? bits - 8 : 0;
+  const uint32_t wlo = w.wlo, wm1 = w.wm1;
+  __syncthreads();  // readers of the previous pass's hist / found are done
+  for (int j = tid; j < 256; j += kRT) sh.hist[j] = 0;
+  if (tid == 0) {
+    sh.found[0] = 0;
+    sh.found[1] = 0;
+  }
+  __syncthreads();
+  if constexpr (kLds) {
+    for (int c = tid; c < nc; c += kRT) {
+      const uint32_t d = sh.candU[c] - wlo;
+      if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const uint32_t d = u[r] - wlo;
+      if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
+      key_fence(r);
+    }
+  }
+  __syncthreads();
+  find_bin(sh, w.kRem);
+  const int bin = sh.found[0] & 255, above = sh.found[1];
+  w.inBin = sh.hist[bin];
+  w.kRem -= above;
+  const uint32_t off = (uint32_t)bin << shift;
+  w.wlo = wlo + off;
+  const uint32_t binM1 = (1u << shift) - 1u, restM1 = wm1 - off;
+  w.wm1 = binM1 < restM1 ? binM1 : restM1;
+  w.shift = shift;
+}
+
 struct Threshold {
   uint32_t T;   // the kSel-th largest key
   int need;     // keys equal to T that are selected (the smallest ids among them)
@@ -219,13 +297,19 @@ template <int KPT>
 __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n, int kSel,
                                                      RegShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // window [lo, hi]: at least kSel keys are >= lo.  From n = 4 * kRT on, every thread holds
-  // real keys and lo is the smallest thread maximum; below, lo is the smallest real key.
-  uint32_t tmax = 0u;
+  // window [lo, hi]: at least kSel keys are >= lo.  Each thread keeps the maxima of its even
+  // and of its odd register groups; from n = 8 * kRT on, both halves of every thread hold
+  // real keys and lo, the smallest of these 2 * kRT = 512 maxima, has a distinct key at or
+  // above it for each of them.  Below that, lo is the smallest real key.
+  uint32_t mA = 0u, mB = 0u;
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) tmax = u[r] > tmax ? u[r] : tmax;
-  uint32_t tmin = tmax;
-  if (n < 4 * kRT) {
+  for (int r = 0; r < KPT; ++r) {
+    if ((r >> 2) & 1) mB = u[r] > mB ? u[r] : mB;
+    else mA = u[r] > mA ? u[r] : mA;
+  }
+  uint32_t tmax = mA > mB ? mA : mB;
+  uint32_t tmin = mA < mB ? mA : mB;
+  if (n < 8 * kRT) {
     tmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
@@ -248,56 +332,33 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     hi = sh.red[0][w] > hi ? sh.red[0][w] : hi;
     lo = sh.red[1][w] < lo ? sh.red[1][w] : lo;
   }
-  uint32_t wlo = lo, wm1 = hi - lo;  // window [wlo, wlo + wm1]
-  int kRem = kSel, nc = -1;
-  for (int pass = 0; pass < 5; ++pass) {
-    const int bits = wm1 ? 32 - __clz(wm1) : 0;
-    const int shift = bits > 8 ? bits - 8 : 0;
-    __syncthreads();  // readers of the previous pass's hist / found are done
-    for (int j = tid; j < 256; j += kRT) sh.hist[j] = 0;
-    if (tid == 0) {
-      sh.found[0] = 0;
-      sh.found[1] = 0;
-    }
-    __syncthreads();
-    if (nc >= 0) {
-      for (int c = tid; c < nc; c += kRT) {
-        const uint32_t d = sh.candU[c] - wlo;
-        if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const uint32_t d = u[r] - wlo;
-        if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
-      }
-    }
-    __syncthreads();
-    find_bin(sh, kRem);
-    const int bin = sh.found[0] & 255, above = sh.found[1];
-    const int inBin = sh.hist[bin];
-    kRem -= above;
-    const uint32_t off = (uint32_t)bin << shift;
-    wlo += off;
-    const uint32_t binM1 = (1u << shift) - 1u, restM1 = wm1 - off;
-    wm1 = binM1 < restM1 ? binM1 : restM1;
-    if (shift == 0) return Threshold{wlo, kRem, inBin, nc};
-    if (nc < 0 && (kSel - kRem) + inBin <= kCandCap) {
-      // keep the keys >= wlo (those above the new window are selected for certain)
-      const uint32_t T = wlo;
-      nc = compact<KPT>(
-          [&](int r) { return u[r] >= T; },
-          [&](int pos, int r) {
-            if (pos < kCandCap) {
-              sh.candU[pos] = u[r];
-              sh.candId[pos] = key_id(r, tid);
-            }
-          },
-          [&] { launder<KPT>(u); }, sh);
-      if (nc > kCandCap) nc = kCandCap;  // cannot happen: the count is exact
-    }
+  RadixWindow w{lo, hi - lo, kSel, 0, 0};
+  radix_pass<KPT, false>(u, 0, w, sh);
+  if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, -1};
+  // keep the keys >= wlo in LDS (those above the new window are selected for certain).  Kept
+  // out of the pass loop below, so that no per-key value of it is hoisted into registers that
+  // stay live across the passes.
+  int nc = -1;
+  if ((kSel - w.kRem) + w.inBin <= kCandCap) {
+    const uint32_t T = w.wlo;
+    const int ft = fresh_tid();
+    nc = compact<KPT>(
+        [&](int r) { return u[r] >= T; },
+        [&](int pos, int r) {
+          if (pos < kCandCap) {
+            sh.candU[pos] = u[r];
+            sh.candId[pos] = key_id(r, ft);
+          }
+        },
+        [&] { launder<KPT>(u); }, sh);
+    if (nc > kCandCap) nc = kCandCap;  // cannot happen: the count is exact
   }
-  return Threshold{wlo, kRem, 0, nc};  // not reached: the shift reaches 0 within 4 passes
+  for (int pass = 1; pass < 5; ++pass) {
+    if (nc >= 0) radix_pass<KPT, true>(u, nc, w, sh);
+    else radix_pass<KPT, false>(u, 0, w, sh);
+    if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, nc};
+  }
+  return Threshold{w.wlo, w.kRem, 0, nc};  // not reached: the shift reaches 0 within 4 passes
 }
 
 // The selected keys in ascending id (registers): above T, then the first `need` keys equal to
@@ -306,10 +367,13 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
 template <int KPT, class Emit>
 __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_t T, int need,
                                                RegShared& sh, Emit emit) {
-  const int tid = threadIdx.x;
+  const int tid = fresh_tid();
   int aboveRun = 0, tieRun = 0;
 #pragma unroll
   for (int g = 0; g < KPT / 4; ++g) {
+    // one group at a time: evaluated ahead, the comparisons of all groups would be held as
+    // lane masks across the scans
+    __builtin_amdgcn_sched_barrier(0);
     bool ab[4], ti[4];
     int packed = 0;
 #pragma unroll
@@ -330,6 +394,46 @@ __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_
         ++a;
       } else if (ti[e]) {
         if (t < need) emit(a + t, key_id(r, tid), u[r]);
+        ++t;
+      }
+    }
+    aboveRun += tot & 0xFFFF;
+    tieRun += tot >> 16;
+  }
+  __syncthreads();
+}
+
+// ordered_select over the row in memory rather than registers: the same selection in
+// ascending id, 1024 keys per step (4 consecutive ids per thread).  Used by prefill only for
+// rows with many keys equal to T, where the cached row is read again.
+template <class Emit>
+__device__ __forceinline__ void ordered_select_row(const float* row, int n, uint32_t T, int need,
+                                                   RegShared& sh, Emit emit) {
+  const int tid = threadIdx.x;
+  int aboveRun = 0, tieRun = 0;
+  for (int base = 0, step = 0; base < n; base += 4 * kRT, ++step) {
+    bool ab[4], ti[4];
+    uint32_t uk[4];
+    int packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = base + 4 * tid + e;
+      uk[e] = id < n ? orderable(row[id]) : 0u;
+      ab[e] = id < n && uk[e] > T;
+      ti[e] = id < n && uk[e] == T;
+      packed += (ab[e] ? 1 : 0) + (ti[e] ? 0x10000 : 0);
+    }
+    int tot;
+    const int ex = block_excl_scan(packed, sh.wcnt[step & 1], &tot);
+    int a = aboveRun + (ex & 0xFFFF), t = tieRun + (ex >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = base + 4 * tid + e;
+      if (ab[e]) {
+        emit(a + (t < need ? t : need), id, uk[e]);
+        ++a;
+      } else if (ti[e]) {
+        if (t < need) emit(a + t, id, uk[e]);
         ++t;
       }
     }
@@ -394,8 +498,13 @@ __device__ __forceinline__ void sort_selected(int m, int kSel, RegShared& sh) {
   __syncthreads();
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kRT) void topk_expand_reg_kernel(TopkArgs a) {
+// Waves per SIMD the register allocation aims for at KPT keys per thread (512 VGPRs per SIMD
+// lane shared by the waves): at most 80 keys leave room for 4 rows of 4 waves on a CU.
+constexpr int reg_waves(int kpt) { return kpt <= 24 ? 5 : kpt <= 80 ? 4 : kpt <= 96 ? 3 : 2; }
+
+template <int KPT, bool kVec>
+__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(reg_waves(KPT))))
+void topk_expand_reg_kernel(TopkArgs a) {
   __shared__ RegShared sh;
   const int tid = threadIdx.x;
   const int64_t i = blockIdx.x, r = a.rowStart + i, b = r / a.S, t = r % a.S;
@@ -409,13 +518,13 @@ __global__ __launch_bounds__(kRT) void topk_expand_reg_kernel(TopkArgs a) {
   const int n = (int)(nVisT < a.numBlocks ? nVisT : a.numBlocks);  // <= kRT * KPT (host)
   const int kSel = n < kTopK ? n : kTopK;
   const float* row = a.logits + i * a.numBlocks;
-  const bool vec = (a.numBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   uint32_t u[KPT];
-  load_keys<KPT>(row, n, vec, u);
+  if (n > 0) load_keys<KPT, kVec>(row, n, u);
   int m;
   if (n <= kTopK) {
+    // every key is taken; ids < n <= 512 all sit in register group 0
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int id = key_id(q, tid);
       if (id < n) sh.sortBuf[id] = composite(u[q], id);
     }
@@ -423,43 +532,38 @@ __global__ __launch_bounds__(kRT) void topk_expand_reg_kernel(TopkArgs a) {
   } else {
     const Threshold th = select_threshold<KPT>(u, n, kSel, sh);
     m = (kSel - th.need) + th.ties;
-    if (m <= 2 * kTopK) {
+    if (th.nc >= 0 && m <= 2 * kTopK) {
+      // the keys >= T are all among the LDS candidates
       const uint32_t T = th.T;
-      if (th.nc >= 0) {
-        const int nc = th.nc;
-        compact<kCandCap / kRT>(
-            [&](int k) {
-              const int q = k * kRT + tid;
-              return q < nc && sh.candU[q] >= T;
-            },
-            [&](int pos, int k) {
-              const int q = k * kRT + tid;
-              if (pos < 2 * kTopK) sh.sortBuf[pos] = composite(sh.candU[q], sh.candId[q]);
-            },
-            [] {}, sh);
-      } else {
-        compact<KPT>([&](int q) { return u[q] >= T; },
-                     [&](int pos, int q) {
-                       if (pos < 2 * kTopK) sh.sortBuf[pos] = composite(u[q], key_id(q, tid));
-                     },
-                     [&] { launder<KPT>(u); }, sh);
-      }
+      const int nc = th.nc;
+      compact<kCandCap / kRT>(
+          [&](int k) {
+            const int q = k * kRT + tid;
+            return q < nc && sh.candU[q] >= T;
+          },
+          [&](int pos, int k) {
+            const int q = k * kRT + tid;
+            if (pos < 2 * kTopK) sh.sortBuf[pos] = composite(sh.candU[q], sh.candId[q]);
+          },
+          [] {}, sh);
     } else {
-      ordered_select<KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t uu) {
+      // many keys equal to T: the exact selection in ascending id, from the row in memory
+      ordered_select_row(row, n, th.T, th.need, sh, [&](int pos, int id, uint32_t uu) {
         if (pos < kTopK) sh.sortBuf[pos] = composite(uu, id);
       });
       m = kSel;
     }
   }
   __syncthreads();
-  if (m <= kTopK) sort_selected<1>(m, kSel, sh);
-  else sort_selected<2>(m, kSel, sh);
+  if (m <= kTopK) sort_selected<kTopK / kRT>(m, kSel, sh);
+  else sort_selected<2 * kTopK / kRT>(m, kSel, sh);
   for (int s = tid; s < 4 * kSel; s += kRT) out[s] = sh.selId[s >> 2] * 4 + (s & 3);
   write_tail_and_pad(out, 4 * kSel, nVisT, (int)((t + 1) % 4), kRT);
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kRT) void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
+template <int KPT, bool kVec>
+__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(reg_waves(KPT))))
+void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
   __shared__ RegShared sh;
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -478,9 +582,8 @@ __global__ __launch_bounds__(kRT) void topk_expand_decode_reg_kernel(TopkDecodeA
     for (int s = tid; s < 4 * n; s += kRT) out[s] = s;  // block s/4, token s%4
   } else {
     const float* row = a.logits + b * a.maxBlocks;
-    const bool vec = (a.maxBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
     uint32_t u[KPT];
-    load_keys<KPT>(row, n, vec, u);
+    load_keys<KPT, kVec>(row, n, u);
     const Threshold th = select_threshold<KPT>(u, n, kSel, sh);
     ordered_select<KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t) {
       if (pos < kTopK) {
@@ -715,7 +818,7 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(ExpandArgs a) {
 // Keys per thread for rows of up to n keys: a multiple of 4 from a short list, or 0 when the
 // row is longer than the register-resident kernels hold.
 int keys_per_thread(int64_t n) {
-  static const int kList[] = {4, 8, 16, 24, 32, 40, 48, 64};
+  static const int kList[] = {4, 8, 16, 24, 32, 48, 64, 72, 96, 128};
   for (int k : kList)
     if (n <= (int64_t)k * kRT) return k;
   return 0;
@@ -736,16 +839,23 @@ hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#define QSA_REG_CASE(KERNEL, K, GRID, ARGS)                                                    \
+  case K:                                                                                      \
+    if (aligned) hipLaunchKernelGGL((KERNEL<K, true>), GRID, dim3(kRT), 0, stream, ARGS);      \
+    else hipLaunchKernelGGL((KERNEL<K, false>), GRID, dim3(kRT), 0, stream, ARGS);             \
+    break;
 #define QSA_REG_CASES(KERNEL, GRID, ARGS)                                                      \
   switch (kpt) {                                                                               \
-    case 4: hipLaunchKernelGGL(KERNEL<4>, GRID, dim3(kRT), 0, stream, ARGS); break;            \
-    case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(kRT), 0, stream, ARGS); break;            \
-    case 16: hipLaunchKernelGGL(KERNEL<16>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
-    case 24: hipLaunchKernelGGL(KERNEL<24>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
-    case 32: hipLaunchKernelGGL(KERNEL<32>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
-    case 40: hipLaunchKernelGGL(KERNEL<40>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
-    case 48: hipLaunchKernelGGL(KERNEL<48>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
-    default: hipLaunchKernelGGL(KERNEL<64>, GRID, dim3(kRT), 0, stream, ARGS); break;          \
+    QSA_REG_CASE(KERNEL, 4, GRID, ARGS)                                                        \
+    QSA_REG_CASE(KERNEL, 8, GRID, ARGS)                                                        \
+    QSA_REG_CASE(KERNEL, 16, GRID, ARGS)                                                       \
+    QSA_REG_CASE(KERNEL, 24, GRID, ARGS)                                                       \
+    QSA_REG_CASE(KERNEL, 32, GRID, ARGS)                                                       \
+    QSA_REG_CASE(KERNEL, 48, GRID, ARGS)                                                       \
+    QSA_REG_CASE(KERNEL, 64, GRID, ARGS)                                                       \
+    QSA_REG_CASE(KERNEL, 72, GRID, ARGS)                                                       \
+    QSA_REG_CASE(KERNEL, 96, GRID, ARGS)                                                       \
+    default: QSA_REG_CASE(KERNEL, 128, GRID, ARGS)                                             \
   }
 
 hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
@@ -754,6 +864,7 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   const int64_t tMax = (r0 / a.S == r1 / a.S) ? r1 % a.S : (int64_t)a.S - 1;
   int64_t nMax = (tMax + 1) / 4;
   if (nMax > a.numBlocks) nMax = a.numBlocks;
+  const bool aligned = (a.numBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   const int kpt = keys_per_thread(nMax);
   const dim3 grid((unsigned)a.numRows);
   if (kpt == 0) {
@@ -765,6 +876,7 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream) {
+  const bool aligned = (a.maxBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   const int kpt = keys_per_thread(a.maxBlocks);
   const dim3 grid((unsigned)a.B);
   if (kpt == 0) {
@@ -776,5 +888,6 @@ hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream
 }
 
 #undef QSA_REG_CASES
+#undef QSA_REG_CASE
 
 }  // namespace qsa
