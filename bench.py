@@ -68,6 +68,28 @@ def survey_bytes(wl):
     return algorithmic_bytes(wl) + 256 * int((L // 4).max())
 
 
+SCORE_ROWS = (65536, 8192)   # the long prefill's query rows [65536, 73728) scored and selected
+INDEX_WIDTH = 2051           # token slots per selected row: 4 * 512 + 3
+
+
+def scores_alg(S, nb, rowStart, numRows):
+    """Algorithmic bytes of one qsa_index_scores call (FP32 logits of every (row, block), the
+    rows' q, the kbar rows any row sees), the visible (row, block) pairs and their flops."""
+    import numpy as np
+    t = rowStart + np.arange(numRows)
+    visible = int(np.minimum((t + 1) // 4, nb).sum())
+    nvis_max = int(min((rowStart + numRows) // 4, nb))
+    return 4 * numRows * nb + 1024 * numRows + 256 * nvis_max, visible, 2 * 4 * 128 * visible
+
+
+def select_alg(S, nb, rowStart, numRows):
+    """Algorithmic bytes of one qsa_index_topk_expand call: each row's complete-block logits
+    read once, its 2051 token slots written."""
+    import numpy as np
+    t = rowStart + np.arange(numRows)
+    return 4 * int(np.minimum((t + 1) // 4, nb).sum()) + 4 * INDEX_WIDTH * numRows
+
+
 def cpu_baseline(wl, reps):
     """The oracle (plain C, OpenMP) on the host: the whole path on the same inputs."""
     import numpy as np
@@ -153,7 +175,7 @@ def _time_stream(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
-def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=65536):
+def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=SCORE_ROWS[0]):
     """Top-512 selection + expand (qsa_index_topk_expand) of the long-prefill rows whose block
     scores the scores leg produced.  Reads each row's complete blocks, writes 2051 indices."""
     import numpy as np
@@ -167,9 +189,7 @@ def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=65536):
                                            S, nb, rowStart, numRows, st)
         assert rc == 0, qsa.qsa_last_error()
     us = _time_stream(torch, call, steps, warmup)
-    t = rowStart + np.arange(numRows)
-    visible = int(np.minimum((t + 1) // 4, nb).sum())
-    alg = 4 * visible + 4 * qsa.INDEX_WIDTH * numRows
+    alg = select_alg(S, nb, rowStart, numRows)
     del out
     return {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks",
             "entry": "qsa_index_topk_expand", "us_per_call": us, "alg_bytes": alg,
@@ -199,7 +219,7 @@ def select_decode_leg(qsa, torch, steps, warmup):
             "GBps": alg / us / 1e3}
 
 
-def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=65536, numRows=8192):
+def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows=SCORE_ROWS[1]):
     """Block scores (qsa_index_scores, MFMA) over a chunk of the long prefill's query rows,
     on the qNormed and kbar the fused prefill produced.  Bound by the FP32 logits it writes."""
     import numpy as np
@@ -219,11 +239,7 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=65536, numRows=8192):
         e1.record(stream)
         torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    t = rowStart + np.arange(numRows)
-    visible = int(np.minimum((t + 1) // 4, nb).sum())
-    nvis_max = int(min((rowStart + numRows) // 4, nb))
-    alg = 4 * numRows * nb + 1024 * numRows + 256 * nvis_max
-    flops = 2 * 4 * 128 * visible
+    alg, visible, flops = scores_alg(S, nb, rowStart, numRows)
     return logits, {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks, "
                         f"bf16, FP32 logits", "entry": "qsa_index_scores", "us_per_call": us,
             "alg_bytes": alg, "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS,
@@ -257,9 +273,9 @@ PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/ptrace -o run -- "
              "python3 $R/bench.py --steps 50 --warmup 10 --no-cpu",
     "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pfetch -o run "
-             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --no-scores --copy-calib",
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
     "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pwrite -o run "
-             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --no-scores --copy-calib",
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
 }
 
 
@@ -318,6 +334,51 @@ def summarize(trace_dir, fetch_dir, write_dir):
            "Written by `python bench.py --summarize gpurun_out/ptrace gpurun_out/pfetch "
            "gpurun_out/pwrite` (also writes `traffic_prefill_kernel_long_prefill.json`)."]
     open(PROFILE_MD, "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+    summarize_next(stats, fetch, write, f_scale, w_scale)
+
+
+NEXT_MD = os.path.join(ROOT, "profiles", "scores_select_long_prefill.md")
+
+
+def summarize_next(stats, fetch, write, f_scale, w_scale):
+    """profiles/ summary of the block-scores and top-512 selection kernels on the long
+    prefill's rows [65536, 73728): durations from the same kernel trace, HBM bytes from the
+    same FETCH_SIZE / WRITE_SIZE runs, against their algorithmic bytes."""
+    S, nb = 131072, 32768
+    r0, nr = SCORE_ROWS
+    legs = [("scores_kernel", "`scores_kernel<Bf16>` (qsa_index_scores)",
+             scores_alg(S, nb, r0, nr)[0]),
+            ("topk_expand_reg_kernel", "`topk_expand_reg_kernel` (qsa_index_topk_expand)",
+             select_alg(S, nb, r0, nr))]
+    md = ["# Block scores and top-512 selection — long prefill rows [65536, 73728) x 32768 "
+          "blocks, bf16", "",
+          "MI355X (gfx950), one GPU.  Kernel durations from the trace, HBM bytes from the "
+          "counter runs of `prefill_kernel_long_prefill.md` (same commands, same scale factors "
+          f"x {f_scale:.3f} for FETCH_SIZE and x {w_scale:.3f} for WRITE_SIZE).", "",
+          "| kernel | avg us | algorithmic bytes | achieved | % of 8 TB/s | measured bytes "
+          "(fetch + write) | vs algorithmic |", "|---|---|---|---|---|---|---|"]
+    for key, label, alg in legs:
+        rows = [r for r in stats if key in r["Name"]]
+        if not rows:
+            continue
+        us = float(rows[0]["AverageNs"]) / 1e3
+        fk = [v for k, v in fetch.items() if key in k]
+        wk = [v for k, v in write.items() if key in k]
+        meas = "—"
+        rel = "—"
+        if fk and wk:
+            mb = fk[0][0] * 1024 * f_scale + wk[0][0] * 1024 * w_scale
+            meas = f"{mb:,.0f} ({fk[0][0] * 1024 * f_scale:,.0f} + {wk[0][0] * 1024 * w_scale:,.0f})"
+            rel = f"{100 * (mb - alg) / alg:+.1f} %"
+        md.append(f"| {label} | {us:.1f} | {alg:,} | {alg / us / 1e6:.2f} TB/s | "
+                  f"{100 * alg / us / 1e6 / 8:.1f} | {meas} | {rel} |")
+    md += ["", "Algorithmic bytes: scores = 4 B per (row, block) logit written + 1024 B of q per "
+           "row + 256 B per kbar row any row sees; selection = 4 B per complete-block logit read "
+           "+ 4 x 2051 B of token slots per row.", "",
+           "Written by `python bench.py --summarize gpurun_out/ptrace gpurun_out/pfetch "
+           "gpurun_out/pwrite`."]
+    open(NEXT_MD, "w").write("\n".join(md) + "\n")
     print("\n".join(md))
 
 
