@@ -90,8 +90,9 @@ def select_alg(S, nb, rowStart, numRows):
     return 4 * int(np.minimum((t + 1) // 4, nb).sum()) + 4 * INDEX_WIDTH * numRows
 
 
-def cpu_baseline(wl, reps):
-    """The oracle (plain C, OpenMP) on the host: the whole path on the same inputs."""
+def cpu_baseline(wl, seconds):
+    """The oracle (plain C, OpenMP) on the host: the whole path on the same inputs, repeated
+    for about `seconds` of CPU work (at least 3 passes); the median pass is reported."""
     import numpy as np
     from oracle.ref import Pool, default
     O = default()
@@ -107,15 +108,17 @@ def cpu_baseline(wl, reps):
 
     run()  # warm-up
     times = []
-    for _ in range(reps):
+    t_start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_start < seconds:
         t0 = time.perf_counter()
         run()
         times.append(time.perf_counter() - t0)
     t = sorted(times)[len(times) // 2]
     return {"value": wl.B * wl.S / t, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole long-prefill workload (B={wl.B}, S={wl.S}) through the oracle's "
-                      f"q_prep + k_compress(pool) + persist, median of {reps} runs after 1 "
-                      f"warm-up, {threads} OpenMP threads; {t * 1e3:.1f} ms per pass"}
+                      f"q_prep + k_compress(pool) + persist, {len(times)} passes in "
+                      f"{time.perf_counter() - t_start:.1f} s after 1 warm-up, median pass "
+                      f"{t * 1e3:.1f} ms, {threads} OpenMP threads"}
 
 
 def decode_leg(qsa, torch, steps, warmup):
@@ -194,6 +197,38 @@ def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=SCORE_ROWS[0]):
     return {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks",
             "entry": "qsa_index_topk_expand", "us_per_call": us, "alg_bytes": alg,
             "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS}
+
+
+def scores_decode_leg(qsa, torch, steps, warmup):
+    """Decode block scores (qsa_index_scores_decode) for the decode workload's 64 sequences,
+    one new token each (contexts up to 32772): kbar gathered from the V-tails of the paged
+    pool.  Latency-bound; reported beside the prefill figure."""
+    import numpy as np
+    from sparse_attention_indexer_qsa_amd import workloads as W
+    wl = W.config4()
+    ctx = (wl.ranges[0] + 1).astype(np.int32)
+    B = len(ctx)
+    mb = int((ctx.max() + 3) // 4)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    q = torch.randn((B, 4, 128), generator=g, device="cuda").to(torch.bfloat16)
+    pool = torch.randn(wl.pool.shape, generator=g, device="cuda", dtype=torch.bfloat16)
+    ps = qsa.PoolState(pool, torch.from_numpy(wl.pool.pageTable).cuda(), wl.pool.numPages,
+                       wl.pool.numKVHeads, wl.pool.poolHeadDim, wl.pool.headSize)
+    pst = ps.c_struct(B)
+    c = torch.from_numpy(ctx).cuda()
+    lg = torch.empty(B, mb, dtype=torch.float32, device="cuda")
+
+    def call(st):
+        rc = qsa.lib.qsa_index_scores_decode(lg.data_ptr(), q.data_ptr(), c.data_ptr(),
+                                             ctypes.byref(pst), B, mb, qsa.QSA_BF16, st)
+        assert rc == 0, qsa.qsa_last_error()
+    us = _time_stream(torch, call, steps, warmup)
+    blocks = int(np.minimum(ctx // 4, mb).sum())
+    alg = 260 * blocks + 1024 * B
+    del pool, ps
+    return {"workload": f"decode, B={B}, context up to {int(ctx.max())}, bf16",
+            "entry": "qsa_index_scores_decode", "us_per_call": us, "alg_bytes": alg,
+            "GBps": alg / us / 1e3}
 
 
 def select_decode_leg(qsa, torch, steps, warmup):
@@ -388,7 +423,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle baseline: seconds of repeated passes (at least 3)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-three-call", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode pre-pass leg")
@@ -507,7 +543,7 @@ def main():
             torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
 
-    scores = select = select_decode = None
+    scores = select = select_decode = scores_decode = None
     if not args.no_scores:
         print("[bench] timing the block scores", file=sys.stderr, flush=True)
         logits, scores = scores_leg(qsa, torch, sets[0], wl, min(args.steps, 50),
@@ -516,6 +552,7 @@ def main():
         select = select_leg(qsa, torch, wl, logits, min(args.steps, 50), min(args.warmup, 5))
         del logits
         select_decode = select_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
+        scores_decode = scores_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
     decode = None
     if not args.no_decode:
         print("[bench] timing the decode pre-pass", file=sys.stderr, flush=True)
@@ -550,11 +587,12 @@ def main():
         "decode_pre_pass": decode,
         "scores": scores,
         "select": select,
+        "scores_decode": scores_decode,
         "select_decode": select_decode,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

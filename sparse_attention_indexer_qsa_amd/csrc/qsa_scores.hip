@@ -261,19 +261,41 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
     widen4(T{}, p.b, qb[h]);
   }
   const float scale = score_scale();
+  // the row's 4 blocks: all page-table entries first, then all V-tail rows, then the dots, so
+  // the two dependent memory latencies are paid once rather than once per block
+  // (the page table is read at a clamped slot unconditionally; the guards of tail_offset -- slot
+  // in range, entry not -1 and inside the pool -- are applied afterwards)
+  const int32_t* vt = a.pool.pageTable + (b * 2 + 1) * a.pool.maxPagesPerSeq;
+  int32_t id[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t slot = (4 * (gBase + 4 * wave + r + 16 * k)) >> 7;
+    id[k] = vt[slot < a.pool.maxPagesPerSeq ? slot : a.pool.maxPagesPerSeq - 1];
+  }
+  int64_t off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t g = gBase + 4 * wave + r + 16 * k, pos = 4 * g;
+    const bool ok = g < nVis && (pos >> 7) < a.pool.maxPagesPerSeq && id[k] >= 0 &&
+                    id[k] < a.pool.numIds;
+    off[k] = ok ? ((int64_t)id[k] * kPageTokens + (pos & (kPageTokens - 1))) * a.pool.rowElems +
+                      a.pool.headSize
+                : -1;
+  }
+  Piece kp[4];  // unconditional loads (a skipped block reads page 0's row, unused)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) kp[k] = load_piece(a.pool.base, off[k] >= 0 ? off[k] : 0, c);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t g = gBase + 4 * wave + r + 16 * k;
     if (g >= nVis) break;
-    const int64_t off = tail_offset(a.pool, b, 1, 4 * g);
-    if (off < 0) {
+    if (off[k] < 0) {  // unused or out-of-range V page entry
       if (c == 0) a.logits[b * a.maxBlocks + g] = -FLT_MAX;
       continue;
     }
-    const Piece kp = load_piece(a.pool.base, off, c);
     float ka[4], kb[4];
-    widen4(T{}, kp.a, ka);
-    widen4(T{}, kp.b, kb);
+    widen4(T{}, kp[k].a, ka);
+    widen4(T{}, kp[k].b, kb);
     float s = 0.0f;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
