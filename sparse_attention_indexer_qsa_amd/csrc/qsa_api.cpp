@@ -353,11 +353,12 @@ QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* 
   a.numBlocks = numBlocks;
   a.rowStart = rowStart;
   a.numRows = numRows;
-  a.tilesPerSeq = ceil_div(seqLen, 32);
+  // the launcher fills the tile fields; bound its workgroup count by 32-token tiles (at most as
+  // many as it uses) of 512 threads
   const int64_t last = (int64_t)rowStart + numRows - 1;
-  a.tile0 = (rowStart / seqLen) * a.tilesPerSeq + (rowStart % seqLen) / 32;
-  a.numTiles = (last / seqLen) * a.tilesPerSeq + (last % seqLen) / 32 - a.tile0 + 1;
-  TRY(check_grid(a.numTiles * ceil_div(numBlocks, 4096)));
+  const int64_t tiles32 = (last / seqLen - rowStart / seqLen) * ceil_div(seqLen, 32) +
+                          (last % seqLen) / 32 - (rowStart % seqLen) / 32 + 1;
+  TRY(check_grid(tiles32 * ceil_div(numBlocks, 4096), 512));
   (void)hipGetLastError();
   return launched(qsa::launch_scores(a, t, static_cast<hipStream_t>(stream)), "qsa_index_scores");
 }

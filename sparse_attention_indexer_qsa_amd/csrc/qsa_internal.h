@@ -94,8 +94,9 @@ struct PreDecodeArgs {
   PoolArgs pool;
 };
 
-// Block scores over global rows [rowStart, rowStart + numRows); workgroup tiles of 32 tokens
-// of one sequence, numTiles of them starting at tile0 (tile = b * tilesPerSeq + t / 32).
+// Block scores over global rows [rowStart, rowStart + numRows).  The launcher fills the tile
+// fields: workgroup tiles of consecutive tokens of one sequence, numTiles of them starting at
+// tile0 (tile = b * tilesPerSeq + t / tokens per tile).
 struct ScoresArgs {
   float* logits;
   const void* qNormed;

@@ -10,11 +10,11 @@
 // Prefill is a dense contraction and runs on MFMA (v_mfma_f32_32x32x16 for bf16 / fp16):
 //  * A operand: 32 rows = 8 consecutive tokens x 4 heads of one sequence.  qNormed is
 //    [B, S, 4, 128], so these 32 head vectors are contiguous and row i = 4*token + head.
-//  * B operand: 32 consecutive kbar rows (blocks).  A workgroup (4 waves, 8 tokens each) keeps
+//  * B operand: 32 consecutive kbar rows (blocks).  A workgroup (8 waves, 8 tokens each) keeps
 //    its q fragments in registers and walks 4096 blocks, 64 at a time staged in LDS
-//    (double-buffered) and shared by the 4 waves; each wave runs the 2 column tiles of a chunk
+//    (double-buffered) and shared by the 8 waves; each wave runs the 2 column tiles of a chunk
 //    on 2 independent accumulators.  64-block chunks keep the LDS at 35 KB and the registers
-//    near 128 per lane, so four workgroups share a CU and hide each other's latency.
+//    below 128 per lane, so two workgroups (4 waves per SIMD) share a CU.
 //  * K = 128 in 8 steps of 16.  Every lane loads A and B with the same lane -> k mapping, so
 //    the dot products do not depend on how the instruction orders k.
 //  * In the 32x32 accumulator a lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32
@@ -41,11 +41,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kSTokWave = 8;                       // tokens per wave
-constexpr int kSTokWG = kSTokWave * kWaves;        // tokens per workgroup (32)
+constexpr int kSWaves = 8;                         // waves per workgroup
+constexpr int kSThreads = 64 * kSWaves;
+constexpr int kSTokWG = kSTokWave * kSWaves;       // tokens per workgroup (64)
 constexpr int kSColTile = 32;                      // blocks per MFMA column tile
 constexpr int kSColTiles = 2;                      // column tiles per staged chunk
 constexpr int kSChunk = kSColTile * kSColTiles;    // blocks staged in LDS at a time (64)
-constexpr int kSPieces = kSChunk * 16 / kThreads;  // 16-byte kbar pieces staged per thread
+constexpr int kSPieces = kSChunk * 16 / kSThreads;  // 16-byte kbar pieces staged per thread
 constexpr int kSRange = 4096;                      // blocks walked by one workgroup
 
 __device__ __forceinline__ float score_scale() { return 1.0f / __builtin_sqrtf(128.0f); }
@@ -73,12 +75,12 @@ __device__ __forceinline__ float relu_head_sum(float d0, float d1, float d2, flo
 }
 
 // Global rows [rowLo, rowHi) of the logits chunk.  Workgroup tile `tile` is tokens
-// [32*(tile % tilesPerSeq), +32) of sequence tile / tilesPerSeq, over one range of 4096
+// [64*(tile % tilesPerSeq), +64) of sequence tile / tilesPerSeq, over one range of 4096
 // blocks, walked in chunks of 64 staged in LDS (double-buffered: the next chunk's loads are in
 // flight while the current one is contracted).  The q fragments of the workgroup's tokens stay
 // in registers for the whole range.
 template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void scores_kernel(ScoresArgs a) {
   // 2 x 64 kbar rows x 256 bytes, rows padded to 272 bytes so that 32 lanes reading one
   // 16-byte piece of 32 different rows spread over the LDS banks
@@ -144,23 +146,18 @@ void scores_kernel(ScoresArgs a) {
   // stored.  Straight-line loads with no zero fill keep the compiler from waiting on them
   // before they are needed.
   const uint16_t* kbSeq = static_cast<const uint16_t*>(a.kbar) + b * nB * (int64_t)kDim;
-  static_assert(kSPieces == 4, "staging holds 4 pieces per thread");
-  const int srow = tid >> 4, spiece = 8 * (tid & 15);  // pieces: rows srow + 16k, k < 4
-  uint4 v0, v1, v2, v3;
+  static_assert(kSPieces == 2, "staging holds 2 pieces per thread");
+  const int srow = tid >> 4, spiece = 8 * (tid & 15);  // pieces: rows srow and srow + 32
+  uint4 v0, v1;
   auto fetch = [&](int c0) {
     const int last = computeHi - 1;
-    const int g0 = min(c0 + srow, last), g1 = min(c0 + srow + 16, last);
-    const int g2 = min(c0 + srow + 32, last), g3 = min(c0 + srow + 48, last);
+    const int g0 = min(c0 + srow, last), g1 = min(c0 + srow + 32, last);
     v0 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g0 * kDim + spiece);
     v1 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g1 * kDim + spiece);
-    v2 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g2 * kDim + spiece);
-    v3 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g3 * kDim + spiece);
   };
   auto stash = [&](int buf) {
     kb_lds[buf][srow][tid & 15] = v0;
-    kb_lds[buf][srow + 16][tid & 15] = v1;
-    kb_lds[buf][srow + 32][tid & 15] = v2;
-    kb_lds[buf][srow + 48][tid & 15] = v3;
+    kb_lds[buf][srow + 32][tid & 15] = v1;
   };
 
   if (rangeLo < computeHi) {
@@ -314,9 +311,16 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
 }  // namespace
 
 hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.numTiles * ((a.numBlocks + kSRange - 1) / kSRange)));
-  if (dt == Dt::BF16) hipLaunchKernelGGL((scores_kernel<Bf16>), grid, dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((scores_kernel<F16>), grid, dim3(kThreads), 0, stream, a);
+  // tiles of kSTokWG tokens covering rows [rowStart, rowStart + numRows)
+  ScoresArgs t = a;
+  t.tilesPerSeq = (a.S + kSTokWG - 1) / kSTokWG;
+  const int64_t last = a.rowStart + a.numRows - 1;
+  t.tile0 = (a.rowStart / a.S) * t.tilesPerSeq + (a.rowStart % a.S) / kSTokWG;
+  t.numTiles = (last / a.S) * t.tilesPerSeq + (last % a.S) / kSTokWG - t.tile0 + 1;
+  const dim3 grid((unsigned)(t.numTiles * ((a.numBlocks + kSRange - 1) / kSRange)));
+  if (dt == Dt::BF16)
+    hipLaunchKernelGGL((scores_kernel<Bf16>), grid, dim3(kSThreads), 0, stream, t);
+  else hipLaunchKernelGGL((scores_kernel<F16>), grid, dim3(kSThreads), 0, stream, t);
   return hipGetLastError();
 }
 
