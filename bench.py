@@ -285,6 +285,31 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows
 COPY_BYTES = 256 << 20
 
 
+def copy_reference(torch, nbytes, steps, warmup, sets=4):
+    """A plain device-to-device copy moving the same bytes as one fused launch (nbytes/2 read,
+    nbytes/2 written), rotated over `sets` buffer pairs and timed with events like the kernel:
+    the streaming rate this machine reaches outside the library, for reading roofline.frac."""
+    n = nbytes // 2 // 4
+    bufs = [(torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0),
+             torch.empty(n, dtype=torch.float32, device="cuda")) for _ in range(sets)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            bufs[i % sets][1].copy_(bufs[i % sets][0])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            bufs[i % sets][1].copy_(bufs[i % sets][0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del bufs
+    return {"what": f"torch copy_ of {n * 4:,} B (read + write = {2 * n * 4:,} B), {sets} "
+                    f"rotating buffer pairs", "us_per_copy": us, "GBps": 2 * n * 4 / us / 1e3,
+            "frac_of_peak": 2 * n * 4 / us / 1e3 / HBM_PEAK_GBPS}
+
+
 def _csv_rows(d, suffix):
     import csv
     import glob
@@ -562,6 +587,8 @@ def main():
 
     alg = algorithmic_bytes(wl)
     achieved = alg / ev / 1e9
+    print("[bench] timing the copy reference", file=sys.stderr, flush=True)
+    copy_ref = copy_reference(torch, alg, min(args.steps, 100), min(args.warmup, 10))
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
@@ -582,7 +609,7 @@ def main():
                    "us_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2],
                                       per[(9 * len(per)) // 10]],
                    "GBps_vs_three_call_bytes": survey_bytes(wl) / ev / 1e9,
-                   "source_sha256_16": kernel_source_hash()},
+                   "source_sha256_16": kernel_source_hash(), "copy_reference": copy_ref},
         "three_call": three,
         "decode_pre_pass": decode,
         "scores": scores,
