@@ -237,9 +237,12 @@ void scores_kernel(ScoresArgs a) {
   }
 }
 
-// Decode: grid (B, ceil(maxBlocks / 64)); DPP row R = 4*wave + r of a workgroup takes blocks
-// g = 64*blockIdx.y + R + 16*k, k < 4.  q of the sequence is held by every row (4 heads x the
-// lane's 8 dims).
+// Decode: grid (B, ceil(maxBlocks / kDecBlocks)); DPP row R = 4*wave + r of a workgroup takes
+// blocks g = kDecBlocks*blockIdx.y + R + 16*k, k < kDecK.  q of the sequence is held by every
+// row (4 heads x the lane's 8 dims).
+constexpr int kDecK = 4;                 // blocks per DPP row (8 measured slower)
+constexpr int kDecBlocks = 16 * kDecK;   // blocks per workgroup
+
 template <class T>
 __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
   const int64_t ctx = a.ctx[b];
   int64_t nVis = ctx > 0 ? ctx / 4 : 0;
   if (nVis > a.maxBlocks) nVis = a.maxBlocks;
-  const int64_t gBase = 64 * (int64_t)blockIdx.y;
+  const int64_t gBase = kDecBlocks * (int64_t)blockIdx.y;
   if (gBase >= nVis) return;
   float qa[4][4], qb[4][4];
 #pragma unroll
@@ -258,20 +261,20 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
     widen4(T{}, p.b, qb[h]);
   }
   const float scale = score_scale();
-  // the row's 4 blocks: all page-table entries first, then all V-tail rows, then the dots, so
+  // the row's kDecK blocks: all page-table entries first, then all V-tail rows, then the dots, so
   // the two dependent memory latencies are paid once rather than once per block
   // (the page table is read at a clamped slot unconditionally; the guards of tail_offset -- slot
   // in range, entry not -1 and inside the pool -- are applied afterwards)
   const int32_t* vt = a.pool.pageTable + (b * 2 + 1) * a.pool.maxPagesPerSeq;
-  int32_t id[4];
+  int32_t id[kDecK];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kDecK; ++k) {
     const int64_t slot = (4 * (gBase + 4 * wave + r + 16 * k)) >> 7;
     id[k] = vt[slot < a.pool.maxPagesPerSeq ? slot : a.pool.maxPagesPerSeq - 1];
   }
-  int64_t off[4];
+  int64_t off[kDecK];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kDecK; ++k) {
     const int64_t g = gBase + 4 * wave + r + 16 * k, pos = 4 * g;
     const bool ok = g < nVis && (pos >> 7) < a.pool.maxPagesPerSeq && id[k] >= 0 &&
                     id[k] < a.pool.numIds;
@@ -279,11 +282,11 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
                       a.pool.headSize
                 : -1;
   }
-  Piece kp[4];  // unconditional loads (a skipped block reads page 0's row, unused)
+  Piece kp[kDecK];  // unconditional loads (a skipped block reads page 0's row, unused)
 #pragma unroll
-  for (int k = 0; k < 4; ++k) kp[k] = load_piece(a.pool.base, off[k] >= 0 ? off[k] : 0, c);
+  for (int k = 0; k < kDecK; ++k) kp[k] = load_piece(a.pool.base, off[k] >= 0 ? off[k] : 0, c);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kDecK; ++k) {
     const int64_t g = gBase + 4 * wave + r + 16 * k;
     if (g >= nVis) break;
     if (off[k] < 0) {  // unused or out-of-range V page entry
@@ -325,7 +328,7 @@ hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream) {
 }
 
 hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream) {
-  const dim3 grid((unsigned)a.B, (unsigned)((a.maxBlocks + 63) / 64));
+  const dim3 grid((unsigned)a.B, (unsigned)((a.maxBlocks + kDecBlocks - 1) / kDecBlocks));
   if (dt == Dt::BF16)
     hipLaunchKernelGGL((scores_decode_kernel<Bf16>), grid, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((scores_decode_kernel<F16>), grid, dim3(kThreads), 0, stream, a);
