@@ -86,9 +86,9 @@ struct RegShared {
 
 __device__ __forceinline__ int key_id(int r, int tid) { return (((r >> 2) * kRT + tid) << 2) + (r & 3); }
 
-// threadIdx.x through an empty asm: per-key ids derived from it in one branch are not merged
-// with (and hoisted above the radix select as) those of another branch, which would hold a
-// register per key across it.
+// threadIdx.x through an empty asm, for per-key id computations: the compiler cannot merge them
+// with those of another code path and hoist them, which would hold registers per key across
+// the radix select (measured: 15 VGPRs at 64 keys per thread in the decode kernel).
 __device__ __forceinline__ int fresh_tid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
@@ -109,8 +109,8 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// The row's keys into registers (padding u = 0), every load issued before any is waited for.
-// kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
+// The row's keys into registers (padding u = 0).  No load sits behind a branch, so the compiler
+// keeps several in flight (a per-group branch had it wait for each load in turn).  kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
 // before n ends inside the row and is one 16-byte load (groups wholly past n load the row's
 // first keys).  Otherwise one load per key at min(id, n - 1).  Keys past n are masked to 0.
 template <int KPT, bool kVec>
@@ -136,13 +136,6 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)
       }
     }
   }
-}
-
-// Keeps the scheduler from interleaving the work of more than 8 register keys at a time: the
-// keys already fill most of the register file, and a long interleave holds a temporary per key.
-// (Called from fully unrolled loops, where r is a constant.)
-__device__ __forceinline__ void key_fence(int r) {
-  if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Exclusive prefix over the block in thread order of a packed pair of small counts
@@ -270,7 +263,6 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, Rad
     for (int r = 0; r < KPT; ++r) {
       const uint32_t d = u[r] - wlo;
       if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
-      key_fence(r);
     }
   }
   __syncthreads();
