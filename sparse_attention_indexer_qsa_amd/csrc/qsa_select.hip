@@ -9,9 +9,10 @@
 // Keys are the monotone map of the FP32 bits, u = bits >= 0 ? bits | 0x80000000 : ~bits; a
 // row's order is descending u, equal u in ascending block id (the stable sort's order).
 //
-// Register-resident rows (up to 128 keys per thread x 256 threads = 32768 blocks):
+// Register-resident rows (prefill: 256 threads, up to 128 keys each; decode: 1024 threads per
+// sequence, up to 32 keys each, which shortens a sequence's latency; 32768 blocks at most):
 //  * The row is read from HBM once, 16 bytes per lane, into registers.  Thread t holds the
-//    ids ((g * 256 + t) * 4 + e) for its register groups g and e < 4.
+//    ids ((g * threads + t) * 4 + e) for its register groups g and e < 4.
 //  * Padding: registers past the row hold u = 0 with ids >= n.  In the (u desc, id asc)
 //    order every padding key comes after every real key, so while kSel <= n the kSel first
 //    keys of the padded row are those of the row, and no step needs to tell them apart.
@@ -50,8 +51,9 @@ namespace {
 constexpr int kTopK = 512;
 constexpr int kIndexWidth = 2051;   // 4 * 512 + 3
 constexpr int kSelThreads = 256;    // streaming kernels
-constexpr int kRT = 256;            // register-resident kernels: threads per row
-constexpr int kRW = kRT / 64;       // waves per row
+constexpr int kRT = 256;            // register-resident prefill kernel: threads per row
+constexpr int kDT = 1024;           // register-resident decode kernel: threads per sequence
+constexpr int kMaxW = kDT / 64;     // most waves of a register-resident workgroup
 constexpr int kCandCap = 2048;      // keys kept in LDS after the first radix pass
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -75,8 +77,8 @@ __device__ __forceinline__ void write_tail_and_pad(int* out, int from, int64_t n
 
 struct RegShared {
   int hist[256];
-  int wcnt[2][kRW];          // per-wave counts (double-buffered by caller's parity)
-  uint32_t red[2][kRW];      // per-wave max / min
+  int wcnt[2][kMaxW];        // per-wave counts (double-buffered by caller's parity)
+  uint32_t red[2][kMaxW];    // per-wave max / min
   int found[2];              // chosen bin, keys above it
   uint32_t candU[kCandCap];
   int32_t candId[kCandCap];
@@ -84,7 +86,9 @@ struct RegShared {
   int32_t selId[kTopK];
 };
 
-__device__ __forceinline__ int key_id(int r, int tid) { return (((r >> 2) * kRT + tid) << 2) + (r & 3); }
+// Id of register key r of thread tid in a workgroup of NT threads.
+template <int NT>
+__device__ __forceinline__ int key_id(int r, int tid) { return (((r >> 2) * NT + tid) << 2) + (r & 3); }
 
 // threadIdx.x through an empty asm, for per-key id computations: the compiler cannot merge them
 // with those of another code path and hoist them, which would hold registers per key across
@@ -113,12 +117,12 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
 // keeps several in flight (a per-group branch had it wait for each load in turn).  kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
 // before n ends inside the row and is one 16-byte load (groups wholly past n load the row's
 // first keys).  Otherwise one load per key at min(id, n - 1).  Keys past n are masked to 0.
-template <int KPT, bool kVec>
+template <int NT, int KPT, bool kVec>
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)[KPT]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int g = 0; g < KPT / 4; ++g) {
-    const int base = (g * kRT + tid) * 4;
+    const int base = (g * NT + tid) * 4;
     const int lim = n - base;  // keys of this group inside the row (<= 0: none)
     if constexpr (kVec) {
       const u32x4 v = __builtin_nontemporal_load(
@@ -140,6 +144,7 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)
 
 // Exclusive prefix over the block in thread order of a packed pair of small counts
 // (low 16 bits, high 16 bits; block totals stay below 65536); *total = block sum.
+template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* slot, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int incl = v;
@@ -152,7 +157,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* slot, int* total) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kRW; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int s = slot[w];
     before += w < wave ? s : 0;
     all += s;
@@ -173,7 +178,7 @@ __device__ __forceinline__ void launder(uint32_t (&u)[KPT]) {
 // Block-wide compaction in an unspecified order: every item k < ITEMS of the thread for which
 // pred(k) holds is passed to store(pos, k) with distinct pos in [0, total); returns the total.
 // refresh() runs between the counting and the storing loop.
-template <int ITEMS, class Pred, class Store, class Refresh>
+template <int NT, int ITEMS, class Pred, class Store, class Refresh>
 __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, RegShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = 0;
@@ -183,7 +188,7 @@ __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, 
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kRW; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int c = sh.wcnt[0][w];
     base += w < wave ? c : 0;
     total += c;
@@ -239,7 +244,7 @@ struct RadixWindow {
 // One radix pass: histogram of the window's keys (registers, or the nc LDS candidates) over
 // 256 bins at a shift that spreads the window over them, then narrow the window to the bin
 // holding the kRem-th largest.
-template <int KPT, bool kLds>
+template <int NT, int KPT, bool kLds>
 __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, RadixWindow& w,
                                            RegShared& sh) {
   const int tid = threadIdx.x;
@@ -247,14 +252,14 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, Rad
   const int shift = bits > 8 ? bits - 8 : 0;
   const uint32_t wlo = w.wlo, wm1 = w.wm1;
   __syncthreads();  // readers of the previous pass's hist / found are done
-  for (int j = tid; j < 256; j += kRT) sh.hist[j] = 0;
+  for (int j = tid; j < 256; j += NT) sh.hist[j] = 0;
   if (tid == 0) {
     sh.found[0] = 0;
     sh.found[1] = 0;
   }
   __syncthreads();
   if constexpr (kLds) {
-    for (int c = tid; c < nc; c += kRT) {
+    for (int c = tid; c < nc; c += NT) {
       const uint32_t d = sh.candU[c] - wlo;
       if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
     }
@@ -285,13 +290,13 @@ struct Threshold {
 };
 
 // Exact radix select of the kSel-th largest key of the (padded) row held in registers, kSel <= n.
-template <int KPT>
+template <int NT, int KPT>
 __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n, int kSel,
                                                      RegShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // window [lo, hi]: at least kSel keys are >= lo.  Each thread keeps the maxima of its even
-  // and of its odd register groups; from n = 8 * kRT on, both halves of every thread hold
-  // real keys and lo, the smallest of these 2 * kRT = 512 maxima, has a distinct key at or
+  // and of its odd register groups; from n = 8 * NT on, both halves of every thread hold
+  // real keys and lo, the smallest of these 2 * NT >= 512 maxima, has a distinct key at or
   // above it for each of them.  Below that, lo is the smallest real key.
   uint32_t mA = 0u, mB = 0u;
 #pragma unroll
@@ -301,11 +306,11 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   }
   uint32_t tmax = mA > mB ? mA : mB;
   uint32_t tmin = mA < mB ? mA : mB;
-  if (n < 8 * kRT) {
+  if (n < 8 * NT) {
     tmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
-      if (key_id(r, tid) < n) tmin = u[r] < tmin ? u[r] : tmin;
+      if (key_id<NT>(r, tid) < n) tmin = u[r] < tmin ? u[r] : tmin;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -320,12 +325,12 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   __syncthreads();
   uint32_t hi = 0u, lo = 0xFFFFFFFFu;
 #pragma unroll
-  for (int w = 0; w < kRW; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     hi = sh.red[0][w] > hi ? sh.red[0][w] : hi;
     lo = sh.red[1][w] < lo ? sh.red[1][w] : lo;
   }
   RadixWindow w{lo, hi - lo, kSel, 0, 0};
-  radix_pass<KPT, false>(u, 0, w, sh);
+  radix_pass<NT, KPT, false>(u, 0, w, sh);
   if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, -1};
   // keep the keys >= wlo in LDS (those above the new window are selected for certain).  Kept
   // out of the pass loop below, so that no per-key value of it is hoisted into registers that
@@ -334,20 +339,20 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   if ((kSel - w.kRem) + w.inBin <= kCandCap) {
     const uint32_t T = w.wlo;
     const int ft = fresh_tid();
-    nc = compact<KPT>(
+    nc = compact<NT, KPT>(
         [&](int r) { return u[r] >= T; },
         [&](int pos, int r) {
           if (pos < kCandCap) {
             sh.candU[pos] = u[r];
-            sh.candId[pos] = key_id(r, ft);
+            sh.candId[pos] = key_id<NT>(r, ft);
           }
         },
         [&] { launder<KPT>(u); }, sh);
     if (nc > kCandCap) nc = kCandCap;  // cannot happen: the count is exact
   }
   for (int pass = 1; pass < 5; ++pass) {
-    if (nc >= 0) radix_pass<KPT, true>(u, nc, w, sh);
-    else radix_pass<KPT, false>(u, 0, w, sh);
+    if (nc >= 0) radix_pass<NT, KPT, true>(u, nc, w, sh);
+    else radix_pass<NT, KPT, false>(u, 0, w, sh);
     if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, nc};
   }
   return Threshold{w.wlo, w.kRem, 0, nc};  // not reached: the shift reaches 0 within 4 passes
@@ -356,7 +361,7 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
 // The selected keys in ascending id (registers): above T, then the first `need` keys equal to
 // T (padding keys have the largest ids and are never among them).  emit(pos, id, u) receives
 // each selected key with its rank pos in ascending id.
-template <int KPT, class Emit>
+template <int NT, int KPT, class Emit>
 __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_t T, int need,
                                                RegShared& sh, Emit emit) {
   const int tid = fresh_tid();
@@ -376,16 +381,16 @@ __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_
       packed += (ab[e] ? 1 : 0) + (ti[e] ? 0x10000 : 0);
     }
     int tot;
-    const int ex = block_excl_scan(packed, sh.wcnt[g & 1], &tot);
+    const int ex = block_excl_scan<NT>(packed, sh.wcnt[g & 1], &tot);
     int a = aboveRun + (ex & 0xFFFF), t = tieRun + (ex >> 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e;
       if (ab[e]) {
-        emit(a + (t < need ? t : need), key_id(r, tid), u[r]);
+        emit(a + (t < need ? t : need), key_id<NT>(r, tid), u[r]);
         ++a;
       } else if (ti[e]) {
-        if (t < need) emit(a + t, key_id(r, tid), u[r]);
+        if (t < need) emit(a + t, key_id<NT>(r, tid), u[r]);
         ++t;
       }
     }
@@ -416,7 +421,7 @@ __device__ __forceinline__ void ordered_select_row(const float* row, int n, uint
       packed += (ab[e] ? 1 : 0) + (ti[e] ? 0x10000 : 0);
     }
     int tot;
-    const int ex = block_excl_scan(packed, sh.wcnt[step & 1], &tot);
+    const int ex = block_excl_scan<kRT>(packed, sh.wcnt[step & 1], &tot);
     int a = aboveRun + (ex & 0xFFFF), t = tieRun + (ex >> 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -511,24 +516,24 @@ void topk_expand_reg_kernel(TopkArgs a) {
   const int kSel = n < kTopK ? n : kTopK;
   const float* row = a.logits + i * a.numBlocks;
   uint32_t u[KPT];
-  if (n > 0) load_keys<KPT, kVec>(row, n, u);
+  if (n > 0) load_keys<kRT, KPT, kVec>(row, n, u);
   int m;
   if (n <= kTopK) {
     // every key is taken; ids < n <= 512 all sit in register group 0
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int id = key_id(q, tid);
+      const int id = key_id<kRT>(q, tid);
       if (id < n) sh.sortBuf[id] = composite(u[q], id);
     }
     m = n;
   } else {
-    const Threshold th = select_threshold<KPT>(u, n, kSel, sh);
+    const Threshold th = select_threshold<kRT, KPT>(u, n, kSel, sh);
     m = (kSel - th.need) + th.ties;
     if (th.nc >= 0 && m <= 2 * kTopK) {
       // the keys >= T are all among the LDS candidates
       const uint32_t T = th.T;
       const int nc = th.nc;
-      compact<kCandCap / kRT>(
+      compact<kRT, kCandCap / kRT>(
           [&](int k) {
             const int q = k * kRT + tid;
             return q < nc && sh.candU[q] >= T;
@@ -554,37 +559,37 @@ void topk_expand_reg_kernel(TopkArgs a) {
 }
 
 template <int KPT, bool kVec>
-__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(reg_waves(KPT))))
+__global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(reg_waves(KPT))))
 void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
   __shared__ RegShared sh;
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
   int32_t* out = a.outIdx + b * kIndexWidth;
   if (a.splitCounters != nullptr)
-    for (int h = tid; h < a.numKVHeads; h += kRT) a.splitCounters[b * a.numKVHeads + h] = 0;
+    for (int h = tid; h < a.numKVHeads; h += kDT) a.splitCounters[b * a.numKVHeads + h] = 0;
   const int64_t c = a.ctx[b];
   if (c <= 0) {
-    for (int s = tid; s < kIndexWidth; s += kRT) out[s] = -1;
+    for (int s = tid; s < kIndexWidth; s += kDT) out[s] = -1;
     return;
   }
   const int64_t nVisC = c / 4;
-  const int n = (int)(nVisC < a.maxBlocks ? nVisC : a.maxBlocks);  // <= kRT * KPT (host)
+  const int n = (int)(nVisC < a.maxBlocks ? nVisC : a.maxBlocks);  // <= kDT * KPT (host)
   const int kSel = n < kTopK ? n : kTopK;
   if (n <= kTopK) {
-    for (int s = tid; s < 4 * n; s += kRT) out[s] = s;  // block s/4, token s%4
+    for (int s = tid; s < 4 * n; s += kDT) out[s] = s;  // block s/4, token s%4
   } else {
     const float* row = a.logits + b * a.maxBlocks;
     uint32_t u[KPT];
-    load_keys<KPT, kVec>(row, n, u);
-    const Threshold th = select_threshold<KPT>(u, n, kSel, sh);
-    ordered_select<KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t) {
+    load_keys<kDT, KPT, kVec>(row, n, u);
+    const Threshold th = select_threshold<kDT, KPT>(u, n, kSel, sh);
+    ordered_select<kDT, KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t) {
       if (pos < kTopK) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) out[4 * pos + j] = 4 * id + j;
       }
     });
   }
-  write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kRT);
+  write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kDT);
 }
 
 // ------------------------------------------------------------------------ streaming ---
@@ -809,10 +814,10 @@ __global__ __launch_bounds__(kSelThreads) void expand_kernel(ExpandArgs a) {
 
 // Keys per thread for rows of up to n keys: a multiple of 4 from a short list, or 0 when the
 // row is longer than the register-resident kernels hold.
-int keys_per_thread(int64_t n) {
+int keys_per_thread(int64_t n, int threads) {
   static const int kList[] = {4, 8, 16, 24, 32, 48, 64, 72, 96, 128};
   for (int k : kList)
-    if (n <= (int64_t)k * kRT) return k;
+    if (k * threads <= 32768 && n <= (int64_t)k * threads) return k;
   return 0;
 }
 
@@ -831,24 +836,11 @@ hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#define QSA_REG_CASE(KERNEL, K, GRID, ARGS)                                                    \
+#define QSA_REG_CASE(KERNEL, K, NTH, GRID, ARGS)                                               \
   case K:                                                                                      \
-    if (aligned) hipLaunchKernelGGL((KERNEL<K, true>), GRID, dim3(kRT), 0, stream, ARGS);      \
-    else hipLaunchKernelGGL((KERNEL<K, false>), GRID, dim3(kRT), 0, stream, ARGS);             \
+    if (aligned) hipLaunchKernelGGL((KERNEL<K, true>), GRID, dim3(NTH), 0, stream, ARGS);      \
+    else hipLaunchKernelGGL((KERNEL<K, false>), GRID, dim3(NTH), 0, stream, ARGS);             \
     break;
-#define QSA_REG_CASES(KERNEL, GRID, ARGS)                                                      \
-  switch (kpt) {                                                                               \
-    QSA_REG_CASE(KERNEL, 4, GRID, ARGS)                                                        \
-    QSA_REG_CASE(KERNEL, 8, GRID, ARGS)                                                        \
-    QSA_REG_CASE(KERNEL, 16, GRID, ARGS)                                                       \
-    QSA_REG_CASE(KERNEL, 24, GRID, ARGS)                                                       \
-    QSA_REG_CASE(KERNEL, 32, GRID, ARGS)                                                       \
-    QSA_REG_CASE(KERNEL, 48, GRID, ARGS)                                                       \
-    QSA_REG_CASE(KERNEL, 64, GRID, ARGS)                                                       \
-    QSA_REG_CASE(KERNEL, 72, GRID, ARGS)                                                       \
-    QSA_REG_CASE(KERNEL, 96, GRID, ARGS)                                                       \
-    default: QSA_REG_CASE(KERNEL, 128, GRID, ARGS)                                             \
-  }
 
 hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   // largest number of complete blocks a row of the chunk can have
@@ -857,29 +849,45 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   int64_t nMax = (tMax + 1) / 4;
   if (nMax > a.numBlocks) nMax = a.numBlocks;
   const bool aligned = (a.numBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
-  const int kpt = keys_per_thread(nMax);
+  const int kpt = keys_per_thread(nMax, kRT);
   const dim3 grid((unsigned)a.numRows);
   if (kpt == 0) {
     hipLaunchKernelGGL(topk_expand_stream_kernel, grid, dim3(kSelThreads), 0, stream, a);
   } else {
-    QSA_REG_CASES(topk_expand_reg_kernel, grid, a)
+    switch (kpt) {
+      QSA_REG_CASE(topk_expand_reg_kernel, 4, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 8, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 16, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 24, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 32, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 48, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 64, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 72, kRT, grid, a)
+      QSA_REG_CASE(topk_expand_reg_kernel, 96, kRT, grid, a)
+      default: QSA_REG_CASE(topk_expand_reg_kernel, 128, kRT, grid, a)
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream) {
   const bool aligned = (a.maxBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
-  const int kpt = keys_per_thread(a.maxBlocks);
+  const int kpt = keys_per_thread(a.maxBlocks, kDT);
   const dim3 grid((unsigned)a.B);
   if (kpt == 0) {
     hipLaunchKernelGGL(topk_expand_decode_stream_kernel, grid, dim3(kSelThreads), 0, stream, a);
   } else {
-    QSA_REG_CASES(topk_expand_decode_reg_kernel, grid, a)
+    switch (kpt) {
+      QSA_REG_CASE(topk_expand_decode_reg_kernel, 4, kDT, grid, a)
+      QSA_REG_CASE(topk_expand_decode_reg_kernel, 8, kDT, grid, a)
+      QSA_REG_CASE(topk_expand_decode_reg_kernel, 16, kDT, grid, a)
+      QSA_REG_CASE(topk_expand_decode_reg_kernel, 24, kDT, grid, a)
+      default: QSA_REG_CASE(topk_expand_decode_reg_kernel, 32, kDT, grid, a)
+    }
   }
   return hipGetLastError();
 }
 
-#undef QSA_REG_CASES
 #undef QSA_REG_CASE
 
 }  // namespace qsa
