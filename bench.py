@@ -142,6 +142,7 @@ def decode_leg(qsa, torch, steps, warmup):
     q = torch.empty(B, S, 4, 128, dtype=torch.int16, device="cuda")
     pst = ps.c_struct(B)
     stream = torch.cuda.Stream()
+    torch.cuda.synchronize()  # inputs made on the default stream are complete
     args = (q.data_ptr(), x.data_ptr(), cs.data_ptr(), cs.shape[0], c.data_ptr(), None,
             wQ.data_ptr(), wK.data_ptr(), wl.eps, ctypes.byref(pst), B, S, qsa.QSA_BF16,
             stream.cuda_stream)
@@ -165,6 +166,7 @@ def decode_leg(qsa, torch, steps, warmup):
 def _time_stream(torch, fn, steps, warmup):
     """Average microseconds per call of fn() on a fresh stream, timed with stream events."""
     stream = torch.cuda.Stream()
+    torch.cuda.synchronize()  # inputs made on the default stream are complete
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn(stream.cuda_stream)
@@ -261,6 +263,7 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows
     S, nb = wl.S, wl.numBlocks
     logits = torch.empty(numRows, nb, dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
+    torch.cuda.synchronize()  # inputs made on the default stream are complete
     args = (logits.data_ptr(), s["q"].data_ptr(), s["kb"].data_ptr(), s["ctx"].data_ptr(), 1, S,
             nb, rowStart, numRows, qsa.QSA_BF16, stream.cuda_stream)
     with torch.cuda.stream(stream):
@@ -275,11 +278,21 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows
         torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     alg, visible, flops = scores_alg(S, nb, rowStart, numRows)
+    # the write floor of this output on this machine: torch fill_ of the same logits tensor
+    fill_us = _time_stream(torch, lambda st: logits.fill_(-3.4028234663852886e38), steps, warmup)
+    out_bytes = logits.numel() * 4
+    write_ref = {"what": f"torch fill_ of the {out_bytes:,} B logits tensor", "us_per_fill": fill_us,
+                 "GBps": out_bytes / fill_us / 1e3,
+                 "frac_of_peak": out_bytes / fill_us / 1e3 / HBM_PEAK_GBPS}
+    # the fills overwrote the logits that the select leg reads: compute them once more
+    with torch.cuda.stream(stream):
+        assert qsa.lib.qsa_index_scores(*args) == 0, qsa.qsa_last_error()
+    torch.cuda.synchronize()
     return logits, {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks, "
                         f"bf16, FP32 logits", "entry": "qsa_index_scores", "us_per_call": us,
             "alg_bytes": alg, "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS,
             "visible_scores": visible, "TFLOPs": flops / us / 1e6,
-            "mfma_bf16_frac": flops / us / 1e6 / 2500.0}
+            "mfma_bf16_frac": flops / us / 1e6 / 2500.0, "write_reference": write_ref}
 
 
 COPY_BYTES = 256 << 20
@@ -293,6 +306,7 @@ def copy_reference(torch, nbytes, steps, warmup, sets=4):
     bufs = [(torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0),
              torch.empty(n, dtype=torch.float32, device="cuda")) for _ in range(sets)]
     stream = torch.cuda.Stream()
+    torch.cuda.synchronize()  # inputs made on the default stream are complete
     with torch.cuda.stream(stream):
         for i in range(warmup):
             bufs[i % sets][1].copy_(bufs[i % sets][0])
@@ -503,6 +517,7 @@ def main():
                            wl.pool.headSize)
         sets.append(dict(x=x, cs=cs, ctx=ctx, pool=ps, q=q, kb=kb, pstruct=ps.c_struct(B)))
     stream = torch.cuda.Stream()
+    torch.cuda.synchronize()  # inputs made on the default stream are complete
     sh = stream.cuda_stream
     L = qsa.lib
 
