@@ -108,11 +108,6 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((unsigned)v, m), hi = __shfl_xor((unsigned)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // The row's keys into registers (padding u = 0).  No load sits behind a branch, so the compiler
 // keeps several in flight (a per-group branch had it wait for each load in turn).  kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
 // before n ends inside the row and is one 16-byte load (groups wholly past n load the row's
@@ -440,6 +435,34 @@ __device__ __forceinline__ void ordered_select_row(const float* row, int n, uint
   __syncthreads();
 }
 
+// Value of lane (lane ^ j) of the wave, j in {1, 2, 4, 8, 16, 32}, by DPP and the permlane
+// swaps (VALU; no LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2;
+// row_half_mirror then quad_perm [3,2,1,0] for 4 (lane ^ 7 ^ 3); row_ror:8 for 8; for 16 and
+// 32 the swap of a register with itself leaves the wanted row (pair) in one of its two results.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int j) {
+  const int lane = threadIdx.x & 63;
+  switch (j) {
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    case 4:
+      return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B,
+                                      0xF, 0xF, false);
+    case 8: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16) ? p[0] : p[1];
+    }
+    default: {
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32) ? p[0] : p[1];
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int j) {
+  return ((uint64_t)xor_lane((uint32_t)(v >> 32), j) << 32) | xor_lane((uint32_t)v, j);
+}
+
 // Bitonic sort, descending, of kRT * E 64-bit values; thread t holds elements e * kRT + t.
 template <int E>
 __device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf) {
@@ -469,7 +492,7 @@ __device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int x = e * kRT + tid;
-          const uint64_t w = j >= 64 ? buf[x ^ j] : shfl_xor64(v[e], j);
+          const uint64_t w = j >= 64 ? buf[x ^ j] : xor_lane64(v[e], j);
           const bool keepMax = ((x & k) == 0) == ((x & j) == 0);
           const bool wBig = w > v[e];
           v[e] = (keepMax == wBig) ? w : v[e];
