@@ -103,6 +103,29 @@ def test_scores_long_prefill_chunk(qsa, O):
         check_logits(got[i:i + 1], ref, bound, f"long row {r0 + i}")
 
 
+def test_scores_long_prefill_bench_rows(qsa, O):
+    """The launch the benchmark times: rows [65536, 73728) of the long prefill against all
+    32768 blocks (128 tiles of 64 tokens x 8 ranges of 4096 blocks).  Every row's mask is
+    checked; 32 sampled rows, the chunk's first and last among them, against the oracle."""
+    wl = W.config3()
+    q, kb = _inputs(O, wl)
+    r0, n = 65536, 8192
+    print(f"[gpu] scores rows [{r0}, {r0 + n}) x {wl.numBlocks}", flush=True)
+    got = _gpu_scores(qsa, q, kb, wl.ctx, wl.dt, r0, n, wl.numBlocks)
+    nvis = (r0 + np.arange(n) + 1) // 4
+    for i0 in range(0, n, 1024):                 # the mask of every row, 1024 rows at a time
+        blk = got[i0:i0 + 1024]
+        masked = blk == NEG
+        assert np.array_equal(masked, np.arange(wl.numBlocks)[None, :] >= nvis[i0:i0 + 1024, None])
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)]))
+    for i in sample:
+        ref = O.scores(q, kb, wl.ctx, r0 + int(i), 1, wl.dt)
+        bound = _abs_bound(q, kb, wl.dt, np.array([r0 + int(i)]), wl.ctx, wl.S)
+        check_logits(got[i:i + 1], ref, bound, f"bench row {r0 + i}")
+    print(f"[parity] scores bench rows: mask of {n} rows, {sample.size} rows vs oracle", flush=True)
+
+
 def test_scores_chunks_and_edges(qsa, O):
     """Ragged S (not a multiple of the 32-token tile), chunks that start mid-tile and span
     sequences, a length-0 sequence: chunks equal slices of one GPU call bit for bit, and match
@@ -124,9 +147,9 @@ def test_scores_chunks_and_edges(qsa, O):
 
 
 def test_scores_decode(qsa, O):
-    """Decode scores of one query token per sequence against V-tails written by a GPU prefill
-    (K1b with the pool); entries past each row's prefix keep their content; unused V pages
-    score -FLT_MAX."""
+    """Decode scores of one query token per sequence against V-tails that the oracle's K1b
+    wrote into a host pool (the same pool bits are uploaded for the GPU call); entries past
+    each row's prefix keep their content; an unused V page entry scores -FLT_MAX."""
     rng = np.random.default_rng(101)
     dt = "bf16"
     L = np.array([4000, 1031, 7, 3, 2048, 513, 0, 64], np.int32)
@@ -141,23 +164,77 @@ def test_scores_decode(qsa, O):
     spec = W.PoolSpec(numPages, pt)
     cs = W.cos_sin_table(Lmax + 8, 1e4)
     nb = (Lmax + 3) // 4
+    rpool = G.oracle_pool(spec)
+    kbh = O.k_compress(x, cs, L, wK, 1e-6, nb, 0, nb, 0, dt, pool=rpool)
     pool = G.device_pool(spec)
-    kbd = torch.empty(B, nb, 128, dtype=torch.int16, device="cuda")
-    qsa.qsa_index_k_compress(kbd, G.dev_bits(x), G.dev(cs), G.dev(L), G.dev_bits(wK), 1e-6, nb,
-                             0, nb, 0, pool=pool, dt=dt)
+    pool.pool.copy_(torch.from_numpy(rpool.data.view(np.int16)))
     qdec = W.to_bits(rng.standard_normal((B, 1, 4, 128), dtype=np.float32), dt)
     out = torch.full((B, nb), float("nan"), device="cuda")
+    print(f"[gpu] scores_decode B={B} maxBlocks={nb}", flush=True)
     qsa.qsa_index_scores_decode(out, G.dev_bits(qdec), G.dev(L), pool, nb, dt=dt)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    from oracle.ref import Pool
-    rpool = Pool(G.host_bits(pool.pool).copy(), pt, numPages, 256)
     ref = O.scores_decode(qdec, L, rpool, nb, dt)
     for b in range(B):
         n = int(L[b]) // 4
         assert np.all(np.isnan(got[b, n:]))
-        kbh = G.host_bits(kbd)
         bound = (1 / np.sqrt(128.0)) * np.einsum(
             "hd,gd->g", np.abs(G.widen(qdec[b, 0], dt)), np.abs(G.widen(kbh[b, :n], dt)))
         check_logits(got[b, :n], ref[b, :n], bound, f"decode seq {b}")
     assert np.all(got[1, 96:128] == NEG)
+
+
+def test_scores_decode_bench_batch(qsa, O):
+    """The launch the benchmark times: the decode batch of 64 sequences (one new token each,
+    contexts up to 32772, rows of (max ctx + 3) / 4 blocks) over the full paged pool of the
+    decode workload (16384 pages per plane, 10 % of the entries unused).  The V pages that six
+    sampled sequences reach hold seeded values, the rest of the pool zeros; those sequences are
+    checked against the oracle on a host pool holding only their pages, renumbered."""
+    wl = W.config4()
+    ctx = (wl.ranges[0] + 1).astype(np.int32)
+    B, mb, dt = len(ctx), int((ctx.max() + 3) // 4), "bf16"
+    spec, hs = wl.pool, wl.pool.headSize
+    rng = np.random.default_rng(61)
+    sample = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)),
+                     *rng.choice(B, 4, replace=False).tolist()})
+    hpt = np.full((len(sample), 2, spec.maxPagesPerSeq), -1, np.int32)
+    dev_pages = []
+    for k, b in enumerate(sample):
+        nvis = min(int(ctx[b]) // 4, mb)
+        for slot in range(min((4 * nvis + 127) // 128, spec.maxPagesPerSeq)):
+            v = int(spec.pageTable[b, 1, slot])
+            if v >= 0:
+                hpt[k, 1, slot] = len(dev_pages)
+                dev_pages.append(v)
+    P = len(dev_pages)
+    tails = W.to_bits(rng.standard_normal((P, 128, 128), dtype=np.float32), dt)
+    from oracle.ref import Pool
+    hdata = np.zeros((2 * ((P + 1) // 2), 128, 1, 128), np.uint16)
+    hdata[:P, :, 0, :] = tails
+    qdec = W.to_bits(rng.standard_normal((B, 1, 4, 128), dtype=np.float32), dt)
+    ref = O.scores_decode(qdec[sample], ctx[sample], Pool(hdata, hpt, (P + 1) // 2, 0), mb, dt)
+    pool = qsa.PoolState(torch.zeros(spec.shape, dtype=torch.int16, device="cuda"),
+                         G.dev(spec.pageTable.astype(np.int32)), spec.numPages,
+                         spec.numKVHeads, spec.poolHeadDim, hs)
+    idx = torch.tensor(dev_pages, dtype=torch.long, device="cuda")
+    pool.pool[idx, :, 0, hs:hs + 128] = torch.from_numpy(tails.view(np.int16)).cuda()
+    out = torch.full((B, mb), float("nan"), device="cuda")
+    print(f"[gpu] scores_decode bench batch B={B} maxBlocks={mb} sampled {sample}", flush=True)
+    qsa.qsa_index_scores_decode(out, G.dev_bits(qdec), G.dev(ctx), pool, mb, dt=dt)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del pool
+    for k, b in enumerate(sample):
+        n = min(int(ctx[b]) // 4, mb)
+        assert np.all(np.isnan(got[b, n:]))
+        kv = np.zeros((n, 128), np.uint16)
+        for g in range(n):
+            slot = (4 * g) // 128
+            h = hpt[k, 1, slot] if slot < spec.maxPagesPerSeq else -1
+            if h >= 0:
+                kv[g] = tails[h, (4 * g) % 128]
+        bound = (1 / np.sqrt(128.0)) * np.einsum(
+            "hd,gd->g", np.abs(G.widen(qdec[b, 0], dt)), np.abs(G.widen(kv, dt)))
+        check_logits(got[b, :n], ref[k, :n], bound, f"bench decode seq {b}")
+    print(f"[parity] scores_decode bench batch: {len(sample)} sampled sequences", flush=True)
+

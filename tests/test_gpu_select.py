@@ -139,6 +139,16 @@ def test_topk_expand_long_rows(qsa, O, case):
     _run_long(qsa, O, *_long_case(case), case)
 
 
+def test_topk_expand_long_prefill_bench_rows(qsa, O):
+    """The launch the benchmark times: rows [65536, 73728) of the long prefill (16384 to 18432
+    complete blocks each, 72 register keys per thread), scores-like logits with recurring
+    values; all 8192 rows bit-exact against the oracle's full stable sort."""
+    S, nb, r0, n = 131072, 32768, 65536, 8192
+    ctx = np.array([S], np.int32)
+    logits = W.prefill_logits(23, ctx, S, nb, r0, n, ("scores",))
+    _run_long(qsa, O, 1, S, nb, ctx, r0, n, logits, "bench rows")
+
+
 def test_topk_expand_all_ones_nan(qsa, O):
     """Keys at the bottom of the order (FP32 bits 0xFFFFFFFF map to 0): a row made only of
     them (the threshold is 0 and padding keys equal it), a row where one thread's keys are all
@@ -201,6 +211,23 @@ def test_topk_expand_decode(qsa, O, maxBlocks):
     bad = np.flatnonzero(np.any(got != ref, axis=1))
     assert bad.size == 0, f"{bad.size} sequences differ, first {bad[0]} (ctx {ctx[bad[0]]})"
     print(f"[parity] topk_expand_decode maxBlocks={maxBlocks}: 64 rows bit-exact", flush=True)
+
+
+def test_topk_expand_decode_bench_batch(qsa, O):
+    """The launch the benchmark times: the decode batch of 64 sequences (one new token each,
+    contexts up to 32772), rows of (max ctx + 3) / 4 blocks, scores-like logits."""
+    wl = W.config4()
+    ctx = (wl.ranges[0] + 1).astype(np.int32)
+    mb = int((ctx.max() + 3) // 4)
+    logits = W.decode_logits(5, ctx, mb, styles=("scores",))
+    ref = O.topk_expand_decode(logits, ctx)
+    out = G.Guarded((len(ctx), WIDTH), torch.int32, fill=POISON)
+    print(f"[gpu] topk_expand_decode bench batch maxBlocks={mb}", flush=True)
+    qsa.qsa_index_topk_expand_decode(out.t, G.dev(logits), G.dev(ctx), mb)
+    got = _host(out)
+    bad = np.flatnonzero(np.any(got != ref, axis=1))
+    assert bad.size == 0, f"{bad.size} sequences differ, first {bad[0]} (ctx {ctx[bad[0]]})"
+    print(f"[parity] topk_expand_decode bench batch: {len(ctx)} rows bit-exact", flush=True)
 
 
 def test_topk_expand_decode_all_ones_nan(qsa, O):
