@@ -211,6 +211,8 @@ int qsa_index_prefill(void* qNormed, void* kbar, const void* indexQk, const floa
  *     keys are not in the pool (page guard fails) is skipped.
  * Positions at or past maxPositions produce +0 q rows and skipped blocks.  Because raw keys are
  * persisted bit-unmodified, decode-time kbar rows equal those of a prefill over the history.
+ * One 256-thread workgroup per sequence; a batch larger than one launch holds is rejected
+ * (QSA_E_INVALID).
  */
 int qsa_index_pre_decode(void* qNormed, const void* indexQk, const float* cosSin,
                          int32_t maxPositions, const int32_t* contextLengths,
@@ -243,7 +245,8 @@ int qsa_index_scores(float* logits, const void* qNormed, const void* kbar,
  * qNormed  [in]  T [B, 1, 4, 128] (one query token per sequence).
  * contextLengths [in] device int32 [B]: TOTAL lengths.   pool: required (kbar is read from the
  * V-tail of token 4g).  Same score as qsa_index_scores; a block whose V page entry is unused
- * or out of range scores -FLT_MAX.  maxBlocks <= 65535*64.
+ * or out of range scores -FLT_MAX.  maxBlocks <= 65535*64.  Grid (B, ceil(maxBlocks/64)) of
+ * 256-thread workgroups; a batch larger than one launch holds is rejected (QSA_E_INVALID).
  */
 int qsa_index_scores_decode(float* logits, const void* qNormed, const int32_t* contextLengths,
                             const qsa_pool_state_t* pool, int32_t batchSize, int32_t maxBlocks,
@@ -297,6 +300,7 @@ int qsa_index_topk_expand(int32_t* outIdx, const float* logits, const int32_t* c
  * tokens then start at 4*maxBlocks); tail = ctx % 4.  nVis <= 512 takes every block 0..nVis-1
  * and reads no logits.  Otherwise the kSel = 512 largest keys of [0, nVis), equal keys at the
  * threshold in ascending id, emitted in ascending block id.  ctx <= 0 gives an all -1 row.
+ * One 1024-thread workgroup per sequence: batchSize <= 2^22 - 1, else QSA_E_INVALID.
  */
 int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits,
                                  const int32_t* contextLengths, int32_t* splitCounters,

@@ -54,8 +54,8 @@ int check_eps(float eps) {
   return QSA_OK;
 }
 
-// Every kernel runs 256-thread workgroups; a launch's x extent counts work-items in 32 bits.
-// A launch holds at most UINT32_MAX threads; `threads` is the workgroup size.
+// A launch's x extent counts work-items in 32 bits, so it holds at most UINT32_MAX threads;
+// `threads` is the workgroup size of the kernel (256 unless stated at the call).
 int check_grid(int64_t workgroups, int64_t threads = 256) {
   if (workgroups > (int64_t)UINT32_MAX / threads)
     return fail(QSA_E_INVALID, "problem needs %lld workgroups, more than one launch can hold",
@@ -316,6 +316,7 @@ QSA_EXPORT int qsa_index_pre_decode(void* qNormed, const void* indexQk, const fl
   TRY(check_eps(rmsEps));
   qsa::PoolArgs p{};
   TRY(check_pool(pool, &p));
+  TRY(check_grid(batchSize));  // one workgroup per sequence
   const qsa::PreDecodeArgs a{qNormed, indexQk, cosSin, maxPositions, contextLengths, newLens,
                              wQ, wK, rmsEps, batchSize, seqLen, p};
   (void)hipGetLastError();
@@ -379,6 +380,7 @@ QSA_EXPORT int qsa_index_scores_decode(float* logits, const void* qNormed,
   TRY(need(contextLengths, "contextLengths", 4));
   qsa::PoolArgs p{};
   TRY(check_pool(pool, &p));
+  TRY(check_grid(batchSize));  // grid (batchSize, ceil(maxBlocks / 64))
   const qsa::ScoresDecodeArgs a{logits, qNormed, contextLengths, p, batchSize, maxBlocks};
   (void)hipGetLastError();
   return launched(qsa::launch_scores_decode(a, t, static_cast<hipStream_t>(stream)),
@@ -461,7 +463,7 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
   if (splitCounters != nullptr) TRY(need(splitCounters, "splitCounters", 4));
   if (maxBlocks > QSA_TOPK) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(batchSize));
+  TRY(check_grid(batchSize, 1024));  // one 1024-thread workgroup per sequence
   const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
                               splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
   (void)hipGetLastError();

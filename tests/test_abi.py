@@ -195,3 +195,78 @@ def test_persist_and_prefill_validation(qsa, host):
     assert pre(dt=2) == qsa.QSA_E_DTYPE
     assert pre(B=0, q=None) == qsa.QSA_OK
     assert "maxPositions" in (pre(P=10) and qsa.qsa_last_error())
+
+
+def test_next_rows_validation(qsa, host):
+    """Decode pre-pass, scores, ids fill, expand and the selections: every invalid argument is
+    rejected with its code before any launch, empty calls return QSA_OK."""
+    L, h, BF = qsa.lib, host, qsa.QSA_BF16
+    pool = ctypes.byref(_pool(qsa, h))
+    E, A, D, OK = qsa.QSA_E_INVALID, qsa.QSA_E_ALIGN, qsa.QSA_E_DTYPE, qsa.QSA_OK
+
+    def pre(**kw):
+        a = dict(q=h.p(0), x=h.p(1), cs=h.p(2), P=64, ctx=h.p(3), nl=None, wq=h.p(4), wk=h.p(8),
+                 eps=1e-6, pool=pool, B=2, S=4, dt=BF)
+        a.update(kw)
+        return L.qsa_index_pre_decode(a["q"], a["x"], a["cs"], a["P"], a["ctx"], a["nl"],
+                                      a["wq"], a["wk"], a["eps"], a["pool"], a["B"], a["S"],
+                                      a["dt"], None)
+    assert pre(dt=3) == D and pre(S=0) == E and pre(P=-1) == E and pre(B=-1) == E
+    assert pre(q=None) == E and pre(x=h.p(1, 2)) == A and pre(nl=h.p(9, 2)) == A
+    assert pre(eps=-1.0) == E and pre(pool=None) == E and pre(B=0, q=None, pool=None) == OK
+    assert pre(B=2**24) == E                                  # more workgroups than a launch
+
+    def sc(**kw):
+        a = dict(lg=h.p(0), q=h.p(1), kb=h.p(2), ctx=h.p(3), B=2, S=64, nb=16, r0=0, n=128, dt=BF)
+        a.update(kw)
+        return L.qsa_index_scores(a["lg"], a["q"], a["kb"], a["ctx"], a["B"], a["S"], a["nb"],
+                                  a["r0"], a["n"], a["dt"], None)
+    assert sc(dt=-2) == D and sc(B=-1) == E and sc(r0=-1) == E and sc(n=-1) == E
+    assert sc(r0=1) == E and sc(n=129) == E                   # chunk past B*S rows
+    assert sc(nb=2**26 + 1) == E and sc(lg=None) == E and sc(q=h.p(1, 8)) == A
+    assert sc(kb=h.p(2, 4)) == A and sc(ctx=h.p(3, 2)) == A and sc(lg=h.p(0, 2)) == A
+    assert sc(n=0, lg=None, q=None) == OK and sc(nb=0, lg=None) == OK
+
+    def scd(**kw):
+        a = dict(lg=h.p(0), q=h.p(1), ctx=h.p(3), pool=pool, B=2, mb=16, dt=BF)
+        a.update(kw)
+        return L.qsa_index_scores_decode(a["lg"], a["q"], a["ctx"], a["pool"], a["B"], a["mb"],
+                                         a["dt"], None)
+    assert scd(dt=9) == D and scd(B=-1) == E and scd(mb=-1) == E and scd(mb=65535 * 64 + 1) == E
+    assert scd(lg=None) == E and scd(q=h.p(1, 2)) == A and scd(pool=None) == E
+    assert scd(B=2**24) == E and scd(B=0, pool=None) == OK and scd(mb=0, lg=None) == OK
+
+    assert L.qsa_index_ids_fill(None, 4, 16, None) == E
+    assert L.qsa_index_ids_fill(h.p(0, 2), 4, 16, None) == A
+    assert L.qsa_index_ids_fill(h.p(0), -1, 16, None) == E
+    assert L.qsa_index_ids_fill(None, 0, 16, None) == OK and L.qsa_index_ids_fill(None, 4, 0, None) == OK
+
+    def ex(**kw):
+        a = dict(out=h.p(0), ids=h.p(1), ctx=h.p(3), B=2, S=64, nb=16, r0=0, n=128)
+        a.update(kw)
+        return L.qsa_index_expand(a["out"], a["ids"], a["ctx"], a["B"], a["S"], a["nb"],
+                                  a["r0"], a["n"], None)
+    assert ex(nb=15) == E                                     # fewer sorted ids than S/4
+    assert ex(S=4096, nb=511, n=64) == E and ex(S=4096, nb=512, n=64, out=None) == E
+    assert ex(r0=100, n=29) == E and ex(out=h.p(0, 2)) == A and ex(ids=None) == E
+    assert ex(S=3, nb=0, n=6, ids=None, r0=0) != E            # no id is read when S/4 = 0
+    assert ex(n=0, out=None) == OK
+
+    def tk(**kw):
+        a = dict(out=h.p(0), lg=h.p(1), ctx=h.p(3), B=2, S=64, nb=16, r0=0, n=128)
+        a.update(kw)
+        return L.qsa_index_topk_expand(a["out"], a["lg"], a["ctx"], a["B"], a["S"], a["nb"],
+                                       a["r0"], a["n"], None)
+    assert tk(B=-1) == E and tk(r0=120, n=9) == E and tk(out=None) == E
+    assert tk(lg=h.p(1, 2)) == A and tk(ctx=None) == E and tk(n=0, out=None) == OK
+
+    def tkd(**kw):
+        a = dict(out=h.p(0), lg=h.p(1), ctx=h.p(3), sc=None, H=0, B=2, mb=1000)
+        a.update(kw)
+        return L.qsa_index_topk_expand_decode(a["out"], a["lg"], a["ctx"], a["sc"], a["H"],
+                                              a["B"], a["mb"], None)
+    assert tkd(B=-1) == E and tkd(mb=-1) == E and tkd(sc=h.p(4), H=-1) == E
+    assert tkd(sc=h.p(4, 2), H=2) == A and tkd(out=None) == E and tkd(lg=None) == E
+    assert tkd(B=2**22) == E                                  # 1024-thread workgroups
+    assert tkd(mb=512, lg=None) != E                          # nVis <= 512 reads no logits
+    assert tkd(B=0, out=None) == OK
