@@ -298,30 +298,41 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows
 COPY_BYTES = 256 << 20
 
 
-def copy_reference(torch, nbytes, steps, warmup, sets=4):
-    """A plain device-to-device copy moving the same bytes as one fused launch (nbytes/2 read,
+def copy_reference(qsa, torch, nbytes, steps, warmup, sets=4):
+    """Plain device-to-device copies moving the same bytes as one fused launch (nbytes/2 read,
     nbytes/2 written), rotated over `sets` buffer pairs and timed with events like the kernel:
-    the streaming rate this machine reaches outside the library, for reading roofline.frac."""
-    n = nbytes // 2 // 4
+    the library's own plain copy (qsa_stream_copy: one 16-byte chunk per thread, non-temporal
+    loads and stores, the fastest copy form measured on this machine) and torch's copy_.  The
+    rate at which this box streams these bytes at all, for reading roofline.frac."""
+    n = nbytes // 2 // 16 * 4
     bufs = [(torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0),
              torch.empty(n, dtype=torch.float32, device="cuda")) for _ in range(sets)]
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()  # inputs made on the default stream are complete
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            bufs[i % sets][1].copy_(bufs[i % sets][0])
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        stream = torch.cuda.Stream()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            bufs[i % sets][1].copy_(bufs[i % sets][0])
-        e1.record(stream)
-        torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i, stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                fn(i, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us = timed(lambda i, st: qsa.qsa_stream_copy(bufs[i % sets][1], bufs[i % sets][0], st))
+    assert torch.equal(bufs[0][1], bufs[0][0]), "qsa_stream_copy did not copy"
+    tus = timed(lambda i, st: bufs[i % sets][1].copy_(bufs[i % sets][0]))
     del bufs
-    return {"what": f"torch copy_ of {n * 4:,} B (read + write = {2 * n * 4:,} B), {sets} "
-                    f"rotating buffer pairs", "us_per_copy": us, "GBps": 2 * n * 4 / us / 1e3,
-            "frac_of_peak": 2 * n * 4 / us / 1e3 / HBM_PEAK_GBPS}
+    moved = 2 * n * 4
+    return {"what": f"qsa_stream_copy of {n * 4:,} B (read + write = {moved:,} B), {sets} "
+                    f"rotating buffer pairs", "us_per_copy": us, "GBps": moved / us / 1e3,
+            "frac_of_peak": moved / us / 1e3 / HBM_PEAK_GBPS,
+            "torch_copy_us": tus, "torch_copy_GBps": moved / tus / 1e3}
 
 
 def _csv_rows(d, suffix):
@@ -603,7 +614,7 @@ def main():
     alg = algorithmic_bytes(wl)
     achieved = alg / ev / 1e9
     print("[bench] timing the copy reference", file=sys.stderr, flush=True)
-    copy_ref = copy_reference(torch, alg, min(args.steps, 100), min(args.warmup, 10))
+    copy_ref = copy_reference(qsa, torch, alg, min(args.steps, 100), min(args.warmup, 10))
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))

@@ -308,6 +308,15 @@ int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits,
                                  void* stream);
 
 /*
+ * Measurement helper, not a step of the indexer: a plain device-to-device copy of `bytes`
+ * (>= 0, a multiple of 16; dst and src 16-byte aligned device buffers that do not overlap),
+ * one 16-byte chunk per thread with non-temporal loads and stores.  The benchmark times it on
+ * the fused launch's traffic to state the rate at which this machine streams bytes at all.
+ * Errors as for every entry point: QSA_E_INVALID / QSA_E_ALIGN before any launch.
+ */
+int qsa_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
  * Debug forms: the same kernels with their FP32 intermediates written out.  Arguments as the
  * entry point of the same name, plus (all device FP32 unless noted, all required):
  *   qsa_debug_q_prep:     meanSq [B,S,4], invRms [B,S,4], preCast [B,S,4,128];

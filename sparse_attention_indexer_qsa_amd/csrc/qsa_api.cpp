@@ -471,6 +471,19 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
                   "qsa_index_topk_expand_decode");
 }
 
+QSA_EXPORT int qsa_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0)
+    return fail(QSA_E_INVALID, "bytes = %lld must be >= 0 and a multiple of 16",
+                (long long)bytes);
+  if (bytes == 0) return ok();
+  TRY(need(dst, "dst", 16));
+  TRY(need(src, "src", 16));
+  TRY(check_grid((bytes / 16 + 255) / 256));
+  (void)hipGetLastError();
+  return launched(qsa::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream)),
+                  "qsa_stream_copy");
+}
+
 QSA_EXPORT const char* qsa_last_error(void) { return g_err; }
 
 QSA_EXPORT int qsa_abi_version(void) { return QSA_ABI_VERSION; }

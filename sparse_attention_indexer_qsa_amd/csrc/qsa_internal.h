@@ -151,6 +151,9 @@ hipError_t launch_pre_decode(const PreDecodeArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_ids_fill(int32_t* ids, int64_t total, int32_t numBlocks, hipStream_t stream);
+
+// Plain copy of `bytes` (a multiple of 16; both pointers 16-byte aligned).
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream);
 hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream);

@@ -57,6 +57,7 @@ def _declare(lib):
         "qsa_index_expand": [P, P, P, I, I, I, I, I, P],
         "qsa_index_topk_expand": [P, P, P, I, I, I, I, I, P],
         "qsa_index_topk_expand_decode": [P, P, P, P, I, I, I, P],
+        "qsa_stream_copy": [P, P, ctypes.c_int64, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -293,6 +294,17 @@ def qsa_index_scores_decode(logits, qNormed, contextLengths, pool, maxBlocks, ba
                                        _dev(contextLengths, "contextLengths", B, _I32),
                                        ctypes.byref(pool.c_struct(B)), B, maxBlocks,
                                        _dt_of(qNormed, dt), _stream(stream)))
+
+
+def qsa_stream_copy(dst, src, stream=None):
+    """Measurement helper: copy all bytes of src into dst (same byte size, a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, src {nbytes}")
+    if nbytes == 0:
+        return
+    _check(lib.qsa_stream_copy(_dev(dst, "dst", 0, (dst.dtype,)), _dev(src, "src", 0, (src.dtype,)),
+                               nbytes, _stream(stream)))
 
 
 def qsa_index_ids_fill(ids, numRows, numBlocks, stream=None):

@@ -270,3 +270,13 @@ def test_next_rows_validation(qsa, host):
     assert tkd(B=2**22) == E                                  # 1024-thread workgroups
     assert tkd(mb=512, lg=None) != E                          # nVis <= 512 reads no logits
     assert tkd(B=0, out=None) == OK
+
+
+def test_stream_copy_validation(qsa, host):
+    L, h = qsa.lib, host
+    assert L.qsa_stream_copy(h.p(0), h.p(1), 24, None) == qsa.QSA_E_INVALID
+    assert L.qsa_stream_copy(h.p(0), h.p(1), -16, None) == qsa.QSA_E_INVALID
+    assert L.qsa_stream_copy(None, h.p(1), 32, None) == qsa.QSA_E_INVALID
+    assert L.qsa_stream_copy(h.p(0, 8), h.p(1), 32, None) == qsa.QSA_E_ALIGN
+    assert L.qsa_stream_copy(h.p(0), h.p(1, 4), 32, None) == qsa.QSA_E_ALIGN
+    assert L.qsa_stream_copy(None, None, 0, None) == qsa.QSA_OK
