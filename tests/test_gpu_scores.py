@@ -146,6 +146,24 @@ def test_scores_chunks_and_edges(qsa, O):
         assert np.array_equal(part.view(np.uint32), full[r0:r0 + n].view(np.uint32)), (r0, n)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_scores_ragged_ranges(qsa, O, dt):
+    """numBlocks = 4103: one full 4096-block range and one of 7 blocks that the last rows of the
+    first sequence reach; a row length that is not a multiple of 4, so the -FLT_MAX fill takes
+    its scalar path; kbar rows beyond every row's reach; two sequences of different lengths;
+    a chunk that crosses from the first sequence into the second mid-tile."""
+    rng = np.random.default_rng(211)
+    B, S, nb = 2, 16390, 4103
+    q = W.to_bits(rng.standard_normal((B, S, 4, 128), dtype=np.float32), dt)
+    kb = W.to_bits(rng.standard_normal((B, nb, 128), dtype=np.float32), dt)
+    ctx = np.array([16390, 9001], np.int32)
+    r0, n = 16000, 800
+    print(f"[gpu] scores ragged ranges {dt} nb={nb} rows [{r0}, {r0 + n})", flush=True)
+    got = _gpu_scores(qsa, q, kb, ctx, dt, r0, n, nb)
+    ref = O.scores(q, kb, ctx, r0, n, dt)
+    check_logits(got, ref, _abs_bound(q, kb, dt, r0 + np.arange(n), ctx, S), f"ragged {dt}")
+
+
 def test_scores_decode(qsa, O):
     """Decode scores of one query token per sequence against V-tails that the oracle's K1b
     wrote into a host pool (the same pool bits are uploaded for the GPU call); entries past
