@@ -60,7 +60,7 @@ def algorithmic_bytes(wl):
     return k1a + k1b + persist + 2 * 256 + 4 * B
 
 
-def survey_bytes(wl):
+def three_call_bytes(wl):
     """The same count with the cosSin rows of block positions counted again for K1b (once
     per call that consumes them, as for the three-call sequence)."""
     import numpy as np
@@ -355,11 +355,11 @@ def _counter(d, name):
 
 PROFILE_MD = os.path.join(ROOT, "profiles", "prefill_kernel_long_prefill.md")
 PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/ptrace -o run -- "
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/ptrace -o run -- "
              "python3 $R/bench.py --steps 50 --warmup 10 --no-cpu",
-    "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pfetch -o run "
+    "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/pfetch -o run "
              "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
-    "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pwrite -o run "
+    "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/pwrite -o run "
              "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
 }
 
@@ -395,7 +395,8 @@ def summarize(trace_dir, fetch_dir, write_dir):
           f"Kernel source hash (first 16 hex of sha256 of `qsa_kernels.hip` + `qsa_device.h`): "
           f"`{kernel_source_hash()}`.  MI355X (gfx950), one GPU.",
           f"Algorithmic bytes per launch: {alg:,}.", "", "## Kernel durations", "",
-          "Command (run from `/tmp` with `TMPDIR=/tmp`; `R` is the repository root):", "",
+          "Command (run from `/tmp` with `TMPDIR=/tmp`; `R` is the repository root, `OUT` the "
+          "directory that collects the profiler output):", "",
           "    " + PROFILE_CMDS["trace"], "",
           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -416,8 +417,8 @@ def summarize(trace_dir, fetch_dir, write_dir):
            f"{wb:,.0f} |", "",
            f"Measured {fb + wb:,.0f} B per launch against {alg:,} algorithmic "
            f"({100 * (fb + wb - alg) / alg:+.2f} %).", "",
-           "Written by `python bench.py --summarize gpurun_out/ptrace gpurun_out/pfetch "
-           "gpurun_out/pwrite` (also writes `traffic_prefill_kernel_long_prefill.json`)."]
+           "Written by `python bench.py --summarize $OUT/ptrace $OUT/pfetch $OUT/pwrite`"
+           " (also writes `traffic_prefill_kernel_long_prefill.json`)."]
     open(PROFILE_MD, "w").write("\n".join(md) + "\n")
     print("\n".join(md))
     summarize_next(stats, fetch, write, f_scale, w_scale)
@@ -461,8 +462,8 @@ def summarize_next(stats, fetch, write, f_scale, w_scale):
     md += ["", "Algorithmic bytes: scores = 4 B per (row, block) logit written + 1024 B of q per "
            "row + 256 B per kbar row any row sees; selection = 4 B per complete-block logit read "
            "+ 4 x 2051 B of token slots per row.", "",
-           "Written by `python bench.py --summarize gpurun_out/ptrace gpurun_out/pfetch "
-           "gpurun_out/pwrite`."]
+           "Written by `python bench.py --summarize $OUT/ptrace $OUT/pfetch $OUT/pwrite`"
+           "."]
     open(NEXT_MD, "w").write("\n".join(md) + "\n")
     print("\n".join(md))
 
@@ -585,7 +586,7 @@ def main():
         print("[bench] timing the three-call sequence", file=sys.stderr, flush=True)
         w3, e3 = timed(lambda i: three_calls(sets[i]), args.steps, args.warmup)
         three = {"ms_per_step": w3 * 1e3, "event_ms_per_step": e3 * 1e3,
-                 "rows_per_s": B * S / w3, "GBps_alg": survey_bytes(wl) / e3 / 1e9}
+                 "rows_per_s": B * S / w3, "GBps_alg": three_call_bytes(wl) / e3 / 1e9}
     if args.copy_calib:
         # a plain streaming kernel of known traffic: reads COPY_BYTES, writes COPY_BYTES
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -634,7 +635,7 @@ def main():
                    "event_us_per_launch": ev * 1e6,
                    "us_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2],
                                       per[(9 * len(per)) // 10]],
-                   "GBps_vs_three_call_bytes": survey_bytes(wl) / ev / 1e9,
+                   "GBps_vs_three_call_bytes": three_call_bytes(wl) / ev / 1e9,
                    "source_sha256_16": kernel_source_hash(), "copy_reference": copy_ref},
         "three_call": three,
         "decode_pre_pass": decode,
