@@ -1,5 +1,6 @@
 // qsa_internal.h — argument blocks and launchers shared by the ABI layer (qsa_api.cpp) and
-// the kernels (qsa_kernels.hip, qsa_scores.hip, qsa_select.hip).  Not part of the public ABI; see include/qsa.h.
+// the kernels (qsa_kernels.hip, qsa_scores.hip, qsa_select.hip, qsa_copy.hip).  Not part of
+// the public ABI, which is include/qsa.h.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -24,16 +24,16 @@
 //    only the keys inside the current window, at a shift that spreads the window over the 256
 //    bins, and a one-wave suffix scan picks the bin holding the kSel-th largest.  The window
 //    holds a few thousand keys of a row (about 512 ln 512 for independent keys), so the bins
-//    are spread and the atomics rarely collide.  After the first pass the keys at or above the chosen bin (a few hundred) are
-//    compacted into LDS and the later passes run on them alone.  The result is the threshold
-//    key T, the number `need` of keys equal to T that are taken (ascending id) and their
-//    count `ties`.
+//    are spread and the atomics rarely collide.  After the first pass the keys at or above
+//    the chosen bin (a few hundred) are compacted into LDS and the later passes run on them
+//    alone.  The result is the threshold key T, the number `need` of keys equal to T that are
+//    taken (ascending id) and their count `ties`.
 //  * Prefill: the keys >= T (kSel - need + ties of them; ties normally = need) are gathered as
 //    64-bit (u, ~id) composites and sorted descending by a bitonic network (strides < 64 by
-//    lane shuffles, 64 and 128 through LDS, larger ones within a thread), so equal keys come
-//    out in ascending id and the first kSel are the result.  More than 1024 such keys (many
-//    equal keys at T), or candidates too many for LDS after the first pass, take the ordered
-//    path below, then the same sort.
+//    DPP moves and permlane swaps, 64 and 128 through LDS, larger ones within a thread), so
+//    equal keys come out in ascending id and the first kSel are the result.  More than 1024
+//    such keys (many equal keys at T), or candidates too many for LDS after the first pass,
+//    take the ordered path below, then the same sort.
 //  * Decode: the selection is emitted in ascending id: one block scan per register group
 //    counts, for each key, the keys above T and the keys equal to T with smaller ids.
 //
@@ -88,7 +88,9 @@ struct RegShared {
 
 // Id of register key r of thread tid in a workgroup of NT threads.
 template <int NT>
-__device__ __forceinline__ int key_id(int r, int tid) { return (((r >> 2) * NT + tid) << 2) + (r & 3); }
+__device__ __forceinline__ int key_id(int r, int tid) {
+  return (((r >> 2) * NT + tid) << 2) + (r & 3);
+}
 
 // threadIdx.x through an empty asm, for per-key id computations: the compiler cannot merge them
 // with those of another code path and hoist them, which would hold registers per key across
@@ -108,8 +110,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// The row's keys into registers (padding u = 0).  No load sits behind a branch, so the compiler
-// keeps several in flight (a per-group branch had it wait for each load in turn).  kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
+// The row's keys into registers (padding u = 0).  No load sits behind a branch, so the
+// compiler keeps several in flight (a per-group branch had it wait for each load in turn).
+// kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
 // before n ends inside the row and is one 16-byte load (groups wholly past n load the row's
 // first keys).  Otherwise one load per key at min(id, n - 1).  Keys past n are masked to 0.
 template <int NT, int KPT, bool kVec>
