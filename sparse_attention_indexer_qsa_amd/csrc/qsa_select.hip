@@ -76,10 +76,10 @@ __device__ __forceinline__ void write_tail_and_pad(int* out, int from, int64_t n
 // ------------------------------------------------------------------ register-resident ---
 
 struct RegShared {
-  int hist[256];
+  int hist[2][256];          // radix histograms, alternating between passes
   int wcnt[2][kMaxW];        // per-wave counts (double-buffered by caller's parity)
   uint32_t red[2][kMaxW];    // per-wave max / min
-  int found[2];              // chosen bin, keys above it
+  int found[2][2];           // per histogram buffer: chosen bin, keys above it
   uint32_t candU[kCandCap];
   int32_t candId[kCandCap];
   uint64_t sortBuf[2 * kTopK];
@@ -203,14 +203,14 @@ __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, 
   return total;
 }
 
-// One wave finds the bin of hist holding the kRem-th largest key (counting from bin 255 down)
-// and the number of keys in bins above it; the block reads them from sh.found after the
-// barrier.
-__device__ __forceinline__ void find_bin(RegShared& sh, int kRem) {
+// One wave finds the bin of histogram buffer p & 1 holding the kRem-th largest key (counting
+// from bin 255 down) and the number of keys in bins above it, into sh.found[p & 1]; the block
+// reads them after the caller's next barrier.
+__device__ __forceinline__ void find_bin(RegShared& sh, int kRem, int p) {
   if (threadIdx.x < 64) {
     const int l = threadIdx.x;
-    const int h0 = sh.hist[4 * l], h1 = sh.hist[4 * l + 1], h2 = sh.hist[4 * l + 2],
-              h3 = sh.hist[4 * l + 3];
+    const int* hist = sh.hist[p & 1];
+    const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
     const int s3 = h3, s2 = h2 + s3, s1 = h1 + s2, s0 = h0 + s1;
     int incl = s0;  // keys in bins >= 4l
 #pragma unroll
@@ -224,11 +224,10 @@ __device__ __forceinline__ void find_bin(RegShared& sh, int kRem) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (cum[q] >= kRem && cum[q] - h[q] < kRem) {
-        sh.found[0] = 4 * l + q;
-        sh.found[1] = cum[q] - h[q];
+        sh.found[p & 1][0] = 4 * l + q;
+        sh.found[p & 1][1] = cum[q] - h[q];
       }
   }
-  __syncthreads();
 }
 
 // Radix window [wlo, wlo + wm1] holding the kRem-th largest of the keys it covers.
@@ -242,36 +241,40 @@ struct RadixWindow {
 // One radix pass: histogram of the window's keys (registers, or the nc LDS candidates) over
 // 256 bins at a shift that spreads the window over them, then narrow the window to the bin
 // holding the kRem-th largest.
+// Pass p histograms into buffer p & 1, which the previous pass (or the caller, for p = 0)
+// cleared; it clears the other buffer for the next pass once every thread is past the barrier
+// that follows the histogram, so no thread still reads it.
 template <int NT, int KPT, bool kLds>
 __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, RadixWindow& w,
-                                           RegShared& sh) {
+                                           RegShared& sh, int p) {
   const int tid = threadIdx.x;
   const int bits = w.wm1 ? 32 - __clz(w.wm1) : 0;
   const int shift = bits > 8 ? bits - 8 : 0;
   const uint32_t wlo = w.wlo, wm1 = w.wm1;
-  __syncthreads();  // readers of the previous pass's hist / found are done
-  for (int j = tid; j < 256; j += NT) sh.hist[j] = 0;
-  if (tid == 0) {
-    sh.found[0] = 0;
-    sh.found[1] = 0;
-  }
-  __syncthreads();
+  int* hist = sh.hist[p & 1];
   if constexpr (kLds) {
     for (int c = tid; c < nc; c += NT) {
       const uint32_t d = sh.candU[c] - wlo;
-      if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
+      if (d <= wm1) atomicAdd(&hist[d >> shift], 1);
     }
   } else {
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const uint32_t d = u[r] - wlo;
-      if (d <= wm1) atomicAdd(&sh.hist[d >> shift], 1);
+      if (d <= wm1) atomicAdd(&hist[d >> shift], 1);
     }
   }
+  __syncthreads();  // the histogram is complete; every thread is done with the previous pass
+  find_bin(sh, w.kRem, p);
+  int* next = sh.hist[(p + 1) & 1];
+  for (int j = tid; j < 256; j += NT) next[j] = 0;
+  if (tid == 0) {
+    sh.found[(p + 1) & 1][0] = 0;
+    sh.found[(p + 1) & 1][1] = 0;
+  }
   __syncthreads();
-  find_bin(sh, w.kRem);
-  const int bin = sh.found[0] & 255, above = sh.found[1];
-  w.inBin = sh.hist[bin];
+  const int bin = sh.found[p & 1][0] & 255, above = sh.found[p & 1][1];
+  w.inBin = hist[bin];
   w.kRem -= above;
   const uint32_t off = (uint32_t)bin << shift;
   w.wlo = wlo + off;
@@ -320,6 +323,11 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     sh.red[0][wave] = tmax;
     sh.red[1][wave] = tmin;
   }
+  for (int j = tid; j < 256; j += NT) sh.hist[0][j] = 0;  // the first pass's histogram
+  if (tid == 0) {
+    sh.found[0][0] = 0;
+    sh.found[0][1] = 0;
+  }
   __syncthreads();
   uint32_t hi = 0u, lo = 0xFFFFFFFFu;
 #pragma unroll
@@ -328,7 +336,7 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     lo = sh.red[1][w] < lo ? sh.red[1][w] : lo;
   }
   RadixWindow w{lo, hi - lo, kSel, 0, 0};
-  radix_pass<NT, KPT, false>(u, 0, w, sh);
+  radix_pass<NT, KPT, false>(u, 0, w, sh, 0);
   if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, -1};
   // keep the keys >= wlo in LDS (those above the new window are selected for certain).  Kept
   // out of the pass loop below, so that no per-key value of it is hoisted into registers that
@@ -349,8 +357,8 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     if (nc > kCandCap) nc = kCandCap;  // cannot happen: the count is exact
   }
   for (int pass = 1; pass < 5; ++pass) {
-    if (nc >= 0) radix_pass<NT, KPT, true>(u, nc, w, sh);
-    else radix_pass<NT, KPT, false>(u, 0, w, sh);
+    if (nc >= 0) radix_pass<NT, KPT, true>(u, nc, w, sh, pass);
+    else radix_pass<NT, KPT, false>(u, 0, w, sh, pass);
     if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, nc};
   }
   return Threshold{w.wlo, w.kRem, 0, nc};  // not reached: the shift reaches 0 within 4 passes
@@ -467,10 +475,14 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int j) {
 }
 
 // Bitonic sort, descending, of kRT * E 64-bit values; thread t holds elements e * kRT + t.
+// The stages with strides 64 and 128 go through LDS, alternating between buf0 and buf1: a
+// stage writes one buffer while others may still read the other, and the barrier of the next
+// stage orders every read of a buffer before it is written again.
 template <int E>
-__device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf) {
+__device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf0, uint64_t* buf1) {
   const int tid = threadIdx.x;
   constexpr int P = kRT * E;
+  int ldsStage = 0;
 #pragma unroll
   for (int k = 2; k <= P; k <<= 1) {
 #pragma unroll
@@ -487,10 +499,12 @@ __device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf) {
           v[e | je] = sw ? x : y;
         }
       } else {
+        uint64_t* buf = (ldsStage & 1) ? buf1 : buf0;
         if (j >= 64) {
 #pragma unroll
           for (int e = 0; e < E; ++e) buf[e * kRT + tid] = v[e];
           __syncthreads();
+          ++ldsStage;
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -500,7 +514,6 @@ __device__ __forceinline__ void sort_desc(uint64_t (&v)[E], uint64_t* buf) {
           const bool wBig = w > v[e];
           v[e] = (keepMax == wBig) ? w : v[e];
         }
-        if (j >= 64) __syncthreads();
       }
     }
   }
@@ -514,7 +527,8 @@ __device__ __forceinline__ void sort_selected(int m, int kSel, RegShared& sh) {
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] = e * kRT + tid < m ? sh.sortBuf[e * kRT + tid] : 0ull;
   __syncthreads();
-  sort_desc<E>(v, sh.sortBuf);
+  // the candidates are consumed by now: their 16 KB hold the second sort buffer
+  sort_desc<E>(v, sh.sortBuf, reinterpret_cast<uint64_t*>(sh.candU));
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (e * kRT + tid < kSel) sh.selId[e * kRT + tid] = (int32_t)~(uint32_t)v[e];
