@@ -106,19 +106,35 @@ def cpu_baseline(wl, seconds):
                      0, wl.dt, pool=pool)
         O.persist(pool, wl.indexQk, None, wl.ctx, wl.numBlocks, 0, wl.numBlocks, 0)
 
-    run()  # warm-up
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or time.perf_counter() - t_start < seconds:
-        t0 = time.perf_counter()
-        run()
-        times.append(time.perf_counter() - t0)
-    t = sorted(times)[len(times) // 2]
+    def timed(budget):
+        run()  # warm-up
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 3 or time.perf_counter() - t_start < budget:
+            t0 = time.perf_counter()
+            run()
+            times.append(time.perf_counter() - t0)
+        return sorted(times)[len(times) // 2], len(times), time.perf_counter() - t_start
+
+    t, passes, spent = timed(seconds)
+    O.set_threads(1)
+    t1, passes1, _ = timed(seconds / 3)
+    O.set_threads(threads)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": wl.B * wl.S / t, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole long-prefill workload (B={wl.B}, S={wl.S}) through the oracle's "
-                      f"q_prep + k_compress(pool) + persist, {len(times)} passes in "
-                      f"{time.perf_counter() - t_start:.1f} s after 1 warm-up, median pass "
-                      f"{t * 1e3:.1f} ms, {threads} OpenMP threads"}
+                      f"q_prep + k_compress(pool) + persist, {passes} passes in {spent:.1f} s "
+                      f"after 1 warm-up, median pass {t * 1e3:.1f} ms, {threads} OpenMP threads",
+            "single_thread": {"value": wl.B * wl.S / t1, "median_pass_ms": t1 * 1e3,
+                              "passes": passes1},
+            "cpu_model": model}
 
 
 def decode_leg(qsa, torch, steps, warmup):
