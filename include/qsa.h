@@ -230,8 +230,9 @@ int qsa_index_pre_decode(void* qNormed, const void* indexQk, const float* cosSin
  * ReLU per head, the scale after the sum; g >= (t+1)/4 (not a complete block up to t) gives
  * -FLT_MAX; a padded row (t >= ctx[b], or ctx[b] <= 0) is -FLT_MAX throughout and its q row is
  * not read.  The dot products run on MFMA; their summation order is the hardware's.
- * numBlocks <= 2^26.  One launch of (64-token tiles of the rows) * ceil(numBlocks/4096)
- * workgroups; a call needing more than 2^24 - 1 of them is rejected (QSA_E_INVALID).
+ * numBlocks <= 2^26.  One launch of (128-token tiles of the rows) * ceil(numBlocks/4096)
+ * workgroups of 512 threads; a call needing more than 2^23 - 1 of them is rejected
+ * (QSA_E_INVALID).
  */
 int qsa_index_scores(float* logits, const void* qNormed, const void* kbar,
                      const int32_t* contextLengths, int32_t batchSize, int32_t seqLen,

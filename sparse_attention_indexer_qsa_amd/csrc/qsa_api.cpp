@@ -338,7 +338,7 @@ QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* 
     return fail(QSA_E_INVALID, "rowStart + numRows = %lld > batchSize * seqLen = %lld",
                 (long long)rowStart + numRows, (long long)rows);
   if (numRows == 0 || numBlocks == 0) return ok();
-  if (numBlocks > (1 << 26))  // the kernel addresses 8 logits rows with 32-bit byte offsets
+  if (numBlocks > (1 << 26))  // the kernel addresses 16 logits rows with 32-bit byte offsets
     return fail(QSA_E_INVALID, "numBlocks = %d exceeds the supported %d", numBlocks, 1 << 26);
   TRY(need(logits, "logits", 4));
   TRY(need(qNormed, "qNormed", 16));
@@ -354,12 +354,8 @@ QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* 
   a.numBlocks = numBlocks;
   a.rowStart = rowStart;
   a.numRows = numRows;
-  // the launcher fills the tile fields; bound its workgroup count by 32-token tiles (at most as
-  // many as it uses) of 512 threads
-  const int64_t last = (int64_t)rowStart + numRows - 1;
-  const int64_t tiles32 = (last / seqLen - rowStart / seqLen) * ceil_div(seqLen, 32) +
-                          (last % seqLen) / 32 - (rowStart % seqLen) / 32 + 1;
-  TRY(check_grid(tiles32 * ceil_div(numBlocks, 4096), 512));
+  qsa::ScoresArgs probe = a;  // the launcher fills the tile fields the same way
+  TRY(check_grid(qsa::scores_workgroups(probe), qsa::kScoresThreads));
   (void)hipGetLastError();
   return launched(qsa::launch_scores(a, t, static_cast<hipStream_t>(stream)), "qsa_index_scores");
 }

@@ -150,6 +150,10 @@ hipError_t launch_persist(const PersistArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_pre_decode(const PreDecodeArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream);
+// Workgroups of the prefill scores launch for a.S, a.numBlocks, a.rowStart, a.numRows (the
+// launcher fills the tile fields the same way), and its threads per workgroup.
+int64_t scores_workgroups(ScoresArgs& a);
+constexpr int kScoresThreads = 512;
 hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_ids_fill(int32_t* ids, int64_t total, int32_t numBlocks, hipStream_t stream);
 

@@ -10,17 +10,18 @@
 // Prefill is a dense contraction and runs on MFMA (v_mfma_f32_32x32x16 for bf16 / fp16):
 //  * A operand: 32 rows = 8 consecutive tokens x 4 heads of one sequence.  qNormed is
 //    [B, S, 4, 128], so these 32 head vectors are contiguous and row i = 4*token + head.
-//  * B operand: 32 consecutive kbar rows (blocks).  A workgroup (8 waves, 8 tokens each) keeps
-//    its q fragments in registers and walks 4096 blocks, 64 at a time staged in LDS
-//    (double-buffered) and shared by the 8 waves; each wave runs the 2 column tiles of a chunk
-//    on 2 independent accumulators.  64-block chunks keep the LDS at 35 KB and the registers
-//    below 128 per lane, so two workgroups (4 waves per SIMD) share a CU.
+//  * B operand: 32 consecutive kbar rows (blocks).  A workgroup (8 waves, 16 tokens each as
+//    two A tiles) keeps its q fragments in registers and walks 4096 blocks, 64 at a time
+//    staged in LDS (double-buffered) and shared by the 8 waves; each kbar fragment a wave
+//    reads from LDS feeds the MFMAs of both its A tiles.  64-block chunks keep the LDS at
+//    35 KB and the registers below 128 per lane, so two workgroups (4 waves per SIMD) share a
+//    CU.
 //  * K = 128 in 8 steps of 16.  Every lane loads A and B with the same lane -> k mapping, so
 //    the dot products do not depend on how the instruction orders k.
 //  * In the 32x32 accumulator a lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32
-//    for its 16 registers v: registers 4m..4m+3 are the four heads of token 2m + lane/32.  ReLU,
-//    the ascending head sum and the scale are in-lane; lanes 0..31 then store 32 consecutive
-//    logits of one token (a 128-byte line) and lanes 32..63 those of the next token.
+//    for its 16 registers v: registers 4m..4m+3 are the four heads of token 2m + lane/32 of
+//    the tile.  ReLU, the ascending head sum and the scale are in-lane; lanes 0..31 then store
+//    32 consecutive logits of one token (a 128-byte line) and lanes 32..63 those of the next.
 //  * Chunks that every token of the wave sees in full take a path without masks; the chunk
 //    holding a token's visibility edge masks per entry.  Column tiles that no token of the
 //    workgroup can see skip the contraction and store -FLT_MAX.  The kernel is bound by the
@@ -40,10 +41,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kSTokWave = 8;                       // tokens per wave
+constexpr int kSTokWave = 16;                      // tokens per wave (two 32-row A tiles)
 constexpr int kSWaves = 8;                         // waves per workgroup
 constexpr int kSThreads = 64 * kSWaves;
-constexpr int kSTokWG = kSTokWave * kSWaves;       // tokens per workgroup (64)
+static_assert(kSThreads == kScoresThreads, "the ABI layer bounds the launch with kScoresThreads");
+constexpr int kSTokWG = kSTokWave * kSWaves;       // tokens per workgroup (128)
 constexpr int kSColTile = 32;                      // blocks per MFMA column tile
 constexpr int kSColTiles = 2;                      // column tiles per staged chunk
 constexpr int kSChunk = kSColTile * kSColTiles;    // blocks staged in LDS at a time (64)
@@ -75,10 +77,11 @@ __device__ __forceinline__ float relu_head_sum(float d0, float d1, float d2, flo
 }
 
 // Global rows [rowLo, rowHi) of the logits chunk.  Workgroup tile `tile` is tokens
-// [64*(tile % tilesPerSeq), +64) of sequence tile / tilesPerSeq, over one range of 4096
+// [128*(tile % tilesPerSeq), +128) of sequence tile / tilesPerSeq, over one range of 4096
 // blocks, walked in chunks of 64 staged in LDS (double-buffered: the next chunk's loads are in
-// flight while the current one is contracted).  The q fragments of the workgroup's tokens stay
-// in registers for the whole range.
+// flight while the current one is contracted).  Each wave holds the q fragments of its 16
+// tokens (two 32-row A tiles) in registers for the whole range, so every kbar fragment it
+// reads from LDS feeds two MFMAs.
 template <class T>
 __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void scores_kernel(ScoresArgs a) {
@@ -110,54 +113,52 @@ void scores_kernel(ScoresArgs a) {
   const int computeHi = nVisWG < rangeHi ? nVisWG : rangeHi;  // contraction needed below
   const float scale = score_scale();
 
-  // A fragments: row i = lane % 32 -> token tw0 + i/4, head i % 4; k-group lane / 32
+  // A fragments of row tile rt: row i = lane % 32 -> token tw0 + 8 rt + i/4, head i % 4;
+  // k-group lane / 32
   const int tw0 = t0 + kSTokWave * wave;
   const int i = lane & 31, kg = lane >> 5;
-  const int tokA = tw0 + (i >> 2);
-  const bool readA = tokA >= tLo && tokA < tHi && tokA < ctx && rangeLo < computeHi;
-  uint4 qa[8];
+  uint4 qa[2][8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    qa[ks] = readA ? load16_u4(a.qNormed,
-                               ((seqRow0 + tokA) * 4 + (i & 3)) * kDim + 16 * ks + 8 * kg)
-                   : make_uint4(0, 0, 0, 0);
-
-  // Output: lane (i, kg) stores block i of each column tile for tokens tw0 + 2m + kg, m < 4,
-  // at byte offset boff[m] from the wave's first row (uniform base; the host bounds numBlocks
-  // so that 8 rows of offsets fit 32 bits)
-  char* waveRow = reinterpret_cast<char*>(a.logits + (seqRow0 + tw0 - rowLo) * (int64_t)nB);
-  uint32_t boff[4];
-  bool live[4];
-  int nVisOut[4];
+  for (int rt = 0; rt < 2; ++rt) {
+    const int tokA = tw0 + 8 * rt + (i >> 2);
+    const bool readA = tokA >= tLo && tokA < tHi && tokA < ctx && rangeLo < computeHi;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int tok = tw0 + 2 * m + kg;
-    live[m] = tok >= tLo && tok < tHi;
-    nVisOut[m] = tok < ctx ? (tok + 1) / 4 : 0;
-    boff[m] = ((uint32_t)(2 * m + kg) * (uint32_t)nB + (uint32_t)i) * 4u;
+    for (int ks = 0; ks < 8; ++ks)
+      qa[rt][ks] = readA ? load16_u4(a.qNormed,
+                                     ((seqRow0 + tokA) * 4 + (i & 3)) * kDim + 16 * ks + 8 * kg)
+                         : make_uint4(0, 0, 0, 0);
   }
-  // chunks below fastHi are seen in full by all 8 tokens of the wave, all of them live
+
+  // Output: in row tile rt, lane (i, kg) holds block i of a column tile for the tokens
+  // tw0 + 8 rt + 2m + kg, m < 4, at byte offset boff + (8 rt + 2m) * rowBytes from the wave's
+  // first row (the host bounds numBlocks so that 16 rows of offsets fit 32 bits)
+  char* waveRow = reinterpret_cast<char*>(a.logits + (seqRow0 + tw0 - rowLo) * (int64_t)nB);
+  const uint32_t boff = ((uint32_t)kg * (uint32_t)nB + (uint32_t)i) * 4u;
+  const uint32_t rowBytes = (uint32_t)nB * 4u;
+  // chunks below fastHi are seen in full by all 16 tokens of the wave, all of them live
   const bool waveLive = tw0 >= tLo && tw0 + kSTokWave <= tHi && tw0 + kSTokWave <= ctx;
   const int fastHi = waveLive ? ((tw0 + 1) / 4 < rangeHi ? (tw0 + 1) / 4 : rangeHi) : 0;
 
-  // staging: 64 rows x 16 pieces per chunk, 4 per thread.  Rows that no token of the
-  // workgroup can see, or past the range, repeat the last row the workgroup can see (fetch
-  // runs only when that row exists): the logits they feed are all masked (-FLT_MAX) or not
-  // stored.  Straight-line loads with no zero fill keep the compiler from waiting on them
-  // before they are needed.
+  // staging: 64 rows x 16 pieces per chunk, rows srow + 32 p for each thread.  Rows
+  // that no token of the workgroup can see, or past the range, repeat the last row the
+  // workgroup can see (fetch runs only when that row exists): the logits they feed are all
+  // masked (-FLT_MAX) or not stored.  Straight-line loads with no zero fill keep the compiler
+  // from waiting on them before they are needed.
   const uint16_t* kbSeq = static_cast<const uint16_t*>(a.kbar) + b * nB * (int64_t)kDim;
-  static_assert(kSPieces == 2, "staging holds 2 pieces per thread");
-  const int srow = tid >> 4, spiece = 8 * (tid & 15);  // pieces: rows srow and srow + 32
-  uint4 v0, v1;
+  constexpr int kRowsPerPass = kSThreads / 16;   // rows staged by one piece index (32)
+  const int srow = tid >> 4, spiece = 8 * (tid & 15);
+  uint4 v[kSPieces];
   auto fetch = [&](int c0) {
     const int last = computeHi - 1;
-    const int g0 = min(c0 + srow, last), g1 = min(c0 + srow + 32, last);
-    v0 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g0 * kDim + spiece);
-    v1 = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g1 * kDim + spiece);
+#pragma unroll
+    for (int p = 0; p < kSPieces; ++p) {
+      const int g = min(c0 + srow + kRowsPerPass * p, last);
+      v[p] = *reinterpret_cast<const uint4*>(kbSeq + (int64_t)g * kDim + spiece);
+    }
   };
   auto stash = [&](int buf) {
-    kb_lds[buf][srow][tid & 15] = v0;
-    kb_lds[buf][srow + 32][tid & 15] = v1;
+#pragma unroll
+    for (int p = 0; p < kSPieces; ++p) kb_lds[buf][srow + kRowsPerPass * p][tid & 15] = v[p];
   };
 
   if (rangeLo < computeHi) {
@@ -176,48 +177,54 @@ void scores_kernel(ScoresArgs a) {
     __syncthreads();  // chunk c0 is in kb_lds[buf]; every wave is done with the other buffer
     const bool more = c0 + kSChunk < computeHi;
     if (more) fetch(c0 + kSChunk);  // in flight during the contraction
-    f32x16 acc[kSColTiles];
+    char* chunkRow = waveRow + 4 * (int64_t)c0;
+    const bool fast = c0 + kSChunk <= fastHi;
 #pragma unroll
-    for (int ct = 0; ct < kSColTiles; ++ct) acc[ct] = f32x16{};
+    for (int ct = 0; ct < kSColTiles; ++ct) {
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int ct = 0; ct < kSColTiles; ++ct)
-        acc[ct] = mfma32(T{}, qa[ks], kb_lds[buf][kSColTile * ct + i][2 * ks + kg], acc[ct]);
-    // epilogue: registers 4m..4m+3 hold the four heads of token 2m + kg for block i of the
-    // column tile; ReLU per head, ascending head sum, scale
-    float x[kSColTiles][4];
-#pragma unroll
-    for (int ct = 0; ct < kSColTiles; ++ct)
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 bk = kb_lds[buf][kSColTile * ct + i][2 * ks + kg];
+        acc0 = mfma32(T{}, qa[0][ks], bk, acc0);
+        acc1 = mfma32(T{}, qa[1][ks], bk, acc1);
+      }
+      // epilogue: registers 4m..4m+3 of tile rt hold the four heads of token 8 rt + 2m + kg
+      // for block i of the column tile; ReLU per head, ascending head sum, scale
+      float x[2][4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        x[ct][m] = scale * relu_head_sum(acc[ct][4 * m], acc[ct][4 * m + 1], acc[ct][4 * m + 2],
-                                         acc[ct][4 * m + 3]);
+        x[0][m] = scale * relu_head_sum(acc0[4 * m], acc0[4 * m + 1], acc0[4 * m + 2],
+                                        acc0[4 * m + 3]);
+        x[1][m] = scale * relu_head_sum(acc1[4 * m], acc1[4 * m + 1], acc1[4 * m + 2],
+                                        acc1[4 * m + 3]);
       }
-    char* chunkRow = waveRow + 4 * (int64_t)c0;
-    if (c0 + kSChunk <= fastHi) {
+      char* tileRow = chunkRow + 4 * kSColTile * ct;
+      if (fast) {
 #pragma unroll
-      for (int ct = 0; ct < kSColTiles; ++ct)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          __builtin_nontemporal_store(
-              x[ct][m], reinterpret_cast<float*>(chunkRow + boff[m] + 4 * kSColTile * ct));
-    } else {
-#pragma unroll
-      for (int ct = 0; ct < kSColTiles; ++ct) {
+          for (int m = 0; m < 4; ++m)
+            __builtin_nontemporal_store(
+                x[rt][m], reinterpret_cast<float*>(tileRow + boff + (8 * rt + 2 * m) * rowBytes));
+      } else {
         const int g = c0 + kSColTile * ct + i;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (live[m] && g < rangeHi)
-            __builtin_nontemporal_store(
-                g < nVisOut[m] ? x[ct][m] : -FLT_MAX,
-                reinterpret_cast<float*>(chunkRow + boff[m] + 4 * kSColTile * ct));
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int tok = tw0 + 8 * rt + 2 * m + kg;
+            const int nVisOut = tok < ctx ? (tok + 1) / 4 : 0;
+            if (tok >= tLo && tok < tHi && g < rangeHi)
+              __builtin_nontemporal_store(
+                  g < nVisOut ? x[rt][m] : -FLT_MAX,
+                  reinterpret_cast<float*>(tileRow + boff + (8 * rt + 2 * m) * rowBytes));
+          }
       }
     }
     if (more) stash(buf ^ 1);
     buf ^= 1;
   }
-  // -FLT_MAX over [fillLo, rangeHi) of each of the wave's 8 token rows, each row written in
+  // -FLT_MAX over [fillLo, rangeHi) of each of the wave's 16 token rows, each row written in
   // contiguous 1 KB runs (64 lanes x 16 bytes)
   const bool vec = (nB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   for (int k = 0; k < kSTokWave; ++k) {
@@ -313,14 +320,18 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
 
 }  // namespace
 
+int64_t scores_workgroups(ScoresArgs& t) {
+  // tiles of kSTokWG tokens covering rows [rowStart, rowStart + numRows), times the ranges
+  t.tilesPerSeq = (t.S + kSTokWG - 1) / kSTokWG;
+  const int64_t last = t.rowStart + t.numRows - 1;
+  t.tile0 = (t.rowStart / t.S) * t.tilesPerSeq + (t.rowStart % t.S) / kSTokWG;
+  t.numTiles = (last / t.S) * t.tilesPerSeq + (last % t.S) / kSTokWG - t.tile0 + 1;
+  return t.numTiles * ((t.numBlocks + kSRange - 1) / kSRange);
+}
+
 hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream) {
-  // tiles of kSTokWG tokens covering rows [rowStart, rowStart + numRows)
   ScoresArgs t = a;
-  t.tilesPerSeq = (a.S + kSTokWG - 1) / kSTokWG;
-  const int64_t last = a.rowStart + a.numRows - 1;
-  t.tile0 = (a.rowStart / a.S) * t.tilesPerSeq + (a.rowStart % a.S) / kSTokWG;
-  t.numTiles = (last / a.S) * t.tilesPerSeq + (last % a.S) / kSTokWG - t.tile0 + 1;
-  const dim3 grid((unsigned)(t.numTiles * ((a.numBlocks + kSRange - 1) / kSRange)));
+  const dim3 grid((unsigned)scores_workgroups(t));
   if (dt == Dt::BF16)
     hipLaunchKernelGGL((scores_kernel<Bf16>), grid, dim3(kSThreads), 0, stream, t);
   else hipLaunchKernelGGL((scores_kernel<F16>), grid, dim3(kSThreads), 0, stream, t);
