@@ -179,10 +179,11 @@ def _drop_entries(rng, pt, frac):
     return pt
 
 
-def config4(B=64, numPages=16384, maxPagesPerSeq=256, max_past=32768):
-    """Decode: 1..4 new tokens per sequence, ranges cover only newly completed blocks."""
+def config4(B=64, numPages=16384, maxPagesPerSeq=256, max_past=32768, dt="bf16"):
+    """Decode: 1..4 new tokens per sequence, ranges cover only newly completed blocks (the same
+    draws for either element type)."""
     rng = np.random.default_rng(4)
-    dt, S = "bf16", 4
+    S = 4
     past = rng.integers(4, max_past + 1, B).astype(np.int32)
     new = rng.integers(1, 5, B).astype(np.int32)
     ctx = (past + new).astype(np.int32)

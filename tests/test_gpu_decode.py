@@ -36,12 +36,12 @@ def _plant_past_keys(rng, wl, data):
                     rng.standard_normal(128, dtype=np.float32), wl.dt)
 
 
-@pytest.mark.parametrize("single", [False, True])
-def test_pre_decode_vs_oracle(qsa, O, single):
+@pytest.mark.parametrize("single,dt", [(False, "bf16"), (True, "bf16"), (False, "f16")])
+def test_pre_decode_vs_oracle(qsa, O, single, dt):
     """A batch of 64 decoding sequences (past lengths up to 8188, 1..4 new tokens each, or one
     with newLens = NULL), pool with 10 % unused entries: q rows within 1 ulp, pool cells equal
     except V-tails within 1 ulp."""
-    wl = W.config4(B=64, numPages=4096, maxPagesPerSeq=64, max_past=8188)
+    wl = W.config4(B=64, numPages=4096, maxPagesPerSeq=64, max_past=8188, dt=dt)
     past, new = wl.ranges[0], wl.ctx - wl.ranges[0]
     if single:
         wl.ctx = (past + 1).astype(np.int32)
@@ -56,7 +56,7 @@ def test_pre_decode_vs_oracle(qsa, O, single):
     pool = G.device_pool(wl.pool)
     pool.pool.copy_(torch.from_numpy(data.view(np.int16)))
     q = G.Guarded((wl.B, wl.S, 4, 128), torch.int16, fill=-1)
-    print(f"[gpu] pre_decode B={wl.B} S={wl.S} single={single}", flush=True)
+    print(f"[gpu] pre_decode B={wl.B} S={wl.S} single={single} {dt}", flush=True)
     qsa.qsa_index_pre_decode(q.t, G.dev_bits(wl.indexQk), G.dev(wl.cosSin), G.dev(wl.ctx),
                              G.dev_bits(wl.wQ), G.dev_bits(wl.wK), wl.eps, pool,
                              newLens=None if single else G.dev(new.astype(np.int32)), dt=wl.dt)
@@ -77,11 +77,11 @@ def test_pre_decode_vs_oracle(qsa, O, single):
     assert written > 0
 
 
-def test_pre_decode_equals_prefill_on_gpu(qsa):
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_pre_decode_equals_prefill_on_gpu(qsa, dt):
     """Prefill of a prefix, then decode steps of 1..4 tokens, all on the GPU, leaves in the
     V-tails exactly the kbar of one GPU prefill over the whole history and yields its q rows."""
     rng = np.random.default_rng(61)
-    dt = "bf16"
     L = np.array([700, 513, 131, 260, 9, 4], np.int32)
     B, Lmax = len(L), int(L.max())
     x = W.to_bits(rng.standard_normal((B, Lmax, 640), dtype=np.float32), dt)

@@ -164,12 +164,12 @@ def test_scores_ragged_ranges(qsa, O, dt):
     check_logits(got, ref, _abs_bound(q, kb, dt, r0 + np.arange(n), ctx, S), f"ragged {dt}")
 
 
-def test_scores_decode(qsa, O):
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_scores_decode(qsa, O, dt):
     """Decode scores of one query token per sequence against V-tails that the oracle's K1b
     wrote into a host pool (the same pool bits are uploaded for the GPU call); entries past
     each row's prefix keep their content; an unused V page entry scores -FLT_MAX."""
     rng = np.random.default_rng(101)
-    dt = "bf16"
     L = np.array([4000, 1031, 7, 3, 2048, 513, 0, 64], np.int32)
     B, Lmax = len(L), int(L.max())
     x = W.to_bits(rng.standard_normal((B, Lmax, 640), dtype=np.float32), dt)
