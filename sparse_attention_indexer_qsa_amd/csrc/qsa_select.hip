@@ -118,6 +118,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 template <int NT, int KPT, bool kVec>
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)[KPT]) {
   const int tid = threadIdx.x;
+  // every load first, into the key registers themselves, so that all of them are in flight
+  // together; the scheduling fence keeps the compiler from mapping (and so waiting for) the
+  // first groups while later loads are still to be issued
 #pragma unroll
   for (int g = 0; g < KPT / 4; ++g) {
     const int base = (g * NT + tid) * 4;
@@ -125,18 +128,23 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)
     if constexpr (kVec) {
       const u32x4 v = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(row + (lim > 0 ? base : 0)));
-      u[4 * g + 0] = lim > 0 ? orderable_bits(v.x) : 0u;
-      u[4 * g + 1] = lim > 1 ? orderable_bits(v.y) : 0u;
-      u[4 * g + 2] = lim > 2 ? orderable_bits(v.z) : 0u;
-      u[4 * g + 3] = lim > 3 ? orderable_bits(v.w) : 0u;
+      u[4 * g + 0] = v.x;
+      u[4 * g + 1] = v.y;
+      u[4 * g + 2] = v.z;
+      u[4 * g + 3] = v.w;
     } else {
       const unsigned* r32 = reinterpret_cast<const unsigned*>(row);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned x = __builtin_nontemporal_load(r32 + min(base + e, n - 1));
-        u[4 * g + e] = lim > e ? orderable_bits(x) : 0u;
-      }
+      for (int e = 0; e < 4; ++e)
+        u[4 * g + e] = __builtin_nontemporal_load(r32 + min(base + e, n - 1));
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < KPT / 4; ++g) {
+    const int lim = n - (g * NT + tid) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[4 * g + e] = lim > e ? orderable_bits(u[4 * g + e]) : 0u;
   }
 }
 
