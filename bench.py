@@ -509,8 +509,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}): the indexer hot path needs no exchange between GPUs, and this build "
-              f"runs and reports a single GPU.", file=sys.stderr)
+              f"{world}): the indexer hot path needs no exchange between GPUs; run it once "
+              f"per GPU, each on its own shard of sequences.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
