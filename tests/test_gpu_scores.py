@@ -164,6 +164,19 @@ def test_scores_ragged_ranges(qsa, O, dt):
     check_logits(got, ref, _abs_bound(q, kb, dt, r0 + np.arange(n), ctx, S), f"ragged {dt}")
 
 
+def test_scores_narrow_numblocks(qsa, O):
+    """numBlocks below a row's complete-block count (kbar holds only the first 50 blocks of a
+    300-token sequence): rows see min((t+1)/4, numBlocks) blocks, the rest of no row exists."""
+    rng = np.random.default_rng(223)
+    dt, B, S, nb = "bf16", 2, 300, 50
+    q = W.to_bits(rng.standard_normal((B, S, 4, 128), dtype=np.float32), dt)
+    kb = W.to_bits(rng.standard_normal((B, nb, 128), dtype=np.float32), dt)
+    ctx = np.array([300, 170], np.int32)
+    got = _gpu_scores(qsa, q, kb, ctx, dt, 0, B * S, nb)
+    ref = O.scores(q, kb, ctx, 0, B * S, dt)
+    check_logits(got, ref, _abs_bound(q, kb, dt, np.arange(B * S), ctx, S), "narrow numBlocks")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_scores_decode(qsa, O, dt):
     """Decode scores of one query token per sequence against V-tails that the oracle's K1b
