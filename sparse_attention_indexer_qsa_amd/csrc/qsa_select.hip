@@ -266,10 +266,12 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, Rad
       if (d <= wm1) atomicAdd(&hist[d >> shift], 1);
     }
   } else {
+    int one = 1;  // the increment in a register the compiler cannot re-create for every key
+    asm volatile("" : "+v"(one));
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const uint32_t d = u[r] - wlo;
-      if (d <= wm1) atomicAdd(&hist[d >> shift], 1);
+      if (d <= wm1) atomicAdd(&hist[d >> shift], one);
     }
   }
   __syncthreads();  // the histogram is complete; every thread is done with the previous pass
@@ -355,14 +357,11 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     const int ft = fresh_tid();
     nc = compact<NT, KPT>(
         [&](int r) { return u[r] >= T; },
-        [&](int pos, int r) {
-          if (pos < kCandCap) {
-            sh.candU[pos] = u[r];
-            sh.candId[pos] = key_id<NT>(r, ft);
-          }
+        [&](int pos, int r) {  // pos < kCandCap: exactly (kSel - kRem) + inBin keys are >= T
+          sh.candU[pos] = u[r];
+          sh.candId[pos] = key_id<NT>(r, ft);
         },
         [&] { launder<KPT>(u); }, sh);
-    if (nc > kCandCap) nc = kCandCap;  // cannot happen: the count is exact
   }
   for (int pass = 1; pass < 5; ++pass) {
     if (nc >= 0) radix_pass<NT, KPT, true>(u, nc, w, sh, pass);
