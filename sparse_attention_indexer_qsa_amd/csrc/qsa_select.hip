@@ -37,9 +37,10 @@
 //  * Decode: the selection is emitted in ascending id: one block scan per register group
 //    counts, for each key, the keys above T and the keys equal to T with smaller ids.
 //
-// Rows longer than 32768 blocks use the streaming kernels at the end of the file (the same
-// radix select with 8-bit digits over the whole key range, the row re-read from L2 on every
-// pass), 256 threads per row.
+// Prefill rows longer than 32768 blocks take the one-wave-per-row kernel (a walk of the row
+// against a running threshold into an LDS candidate buffer, below).  Decode rows that long
+// take the streaming kernel at the end of the file (the same radix select with 8-bit digits
+// over the whole key range, the row re-read from L2 on every pass), 256 threads per row.
 
 #include <float.h>
 
@@ -639,6 +640,370 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
   write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kDT);
 }
 
+// -------------------------------------------------------------------- one wave per row ---
+//
+// Prefill rows longer than 32768 blocks.  Each wave of a workgroup takes a row of its own and walks it
+// front to back, a step of keys at a time, against a running threshold thr: a wave-private
+// LDS buffer holds candidates {u, id}; whenever the next step's keys above thr would not fit,
+// the buffer is cut to a few more than its 512 largest (u desc, id asc), all of them at or
+// above some value lo, and thr becomes lo.  Later keys have larger ids, so one of them can be
+// among a prefix's 512 largest only if u > thr: equal u loses the tie.  The buffer therefore
+// always holds the 512 largest keys seen so far; at the end it is cut to exactly those 512,
+// which are sorted in registers.  No workgroup barrier: the waves of a workgroup share
+// nothing, and several rows per CU overlap their loads with the others' selection.
+
+constexpr int kWaveRows = 4;       // rows (waves) per workgroup of the one-wave-per-row kernel
+constexpr int kWaveCap = 1536;     // candidate buffer entries per row (12 rows per CU)
+constexpr int kWaveKPL = 8;        // keys per lane per step (512 keys)
+
+template <int kCap>
+struct WaveShared {
+  uint32_t u[kCap];  // candidates: key
+  uint32_t id[kCap]; //             block id
+  int hist[256];
+};
+
+// Orders this wave's LDS accesses in program order (a wave's LDS instructions execute in
+// issue order; the fence keeps the compiler from moving one across another).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int j = 1; j < 64; j <<= 1) {
+    const uint32_t w = xor_lane(v, j);
+    v = w > v ? w : v;
+  }
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int j = 1; j < 64; j <<= 1) {
+    const uint32_t w = xor_lane(v, j);
+    v = w < v ? w : v;
+  }
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Radix select of the kRem-th largest of the wave's valid keys (SL per lane: key(i, c, valid)
+// with c the entry count), inside the window [lo, lo + m1] that holds all of them: each pass
+// histograms the window's keys over 256 bins (LDS atomics) at a shift that spreads the window
+// over the bins, and narrows the window to the bin holding the kRem-th largest.  Stops once
+// that bin holds at most `slack` keys more than are still to be taken, or is a single value.
+// On return lo is the bin's base, kRem the number of its keys still to take (every key above
+// the bin is taken) and inBin its count.
+template <int SL, class Key>
+__device__ __forceinline__ void wave_window_select(Key key, int cnt, int* hist, uint32_t& lo,
+                                                   uint32_t m1, int& kRem, int& inBin,
+                                                   int slack) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll 1
+  for (int pass = 0; pass < 5; ++pass) {
+    // the entry count through an empty asm: the per-slot validity masks are evaluated again in
+    // every pass rather than hoisted out of the loop and held (one SGPR pair per slot)
+    int c = cnt;
+    asm volatile("" : "+v"(c));
+    const int bits = m1 ? 32 - __clz(m1) : 0;
+    const int shift = bits > 8 ? bits - 8 : 0;
+    *reinterpret_cast<int4*>(&hist[4 * lane]) = make_int4(0, 0, 0, 0);
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      bool valid;
+      const uint32_t d = key(i, c, valid) - lo;
+      if (valid && d <= m1) atomicAdd(&hist[d >> shift], 1);
+    }
+    wave_sync();
+    // lane l holds bins 4l .. 4l + 3; suffix sums over the lanes from bin 255 down
+    const int4 h = *reinterpret_cast<const int4*>(&hist[4 * lane]);
+    const int s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
+    int incl = s0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_down(incl, o);
+      if (lane + o < 64) incl += t;
+    }
+    const int ex = incl - s0;  // keys in bins >= 4l + 4
+    const int cum[4] = {ex + s0, ex + s1, ex + s2, ex + s3};
+    const int hq[4] = {h.x, h.y, h.z, h.w};
+    int myBin = 0, myAbove = 0, myIn = 0;
+    bool hit = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (cum[q] >= kRem && cum[q] - hq[q] < kRem) {
+        myBin = 4 * lane + q;
+        myAbove = cum[q] - hq[q];
+        myIn = hq[q];
+        hit = true;
+      }
+    const uint64_t m = __ballot(hit);
+    const int src = m ? (int)__builtin_ctzll(m) : 0;
+    const int bin = __builtin_amdgcn_readlane(myBin, src);
+    kRem -= __builtin_amdgcn_readlane(myAbove, src);
+    inBin = __builtin_amdgcn_readlane(myIn, src);
+    const uint32_t off = (uint32_t)bin << shift;
+    lo += off;
+    const uint32_t binM1 = (1u << shift) - 1u, restM1 = m1 - off;
+    m1 = binM1 < restM1 ? binM1 : restM1;
+    if (inBin - kRem <= slack || shift == 0) return;
+  }
+}
+
+// Cut the wave's buffer (cnt > K entries) in place to its K largest (u desc, id asc), or, with
+// slack > 0, to at most K + slack entries that include them: every entry at or above a value
+// lo.  Sets cnt to the entries kept and returns the threshold that later keys, with larger
+// ids, must exceed: the u of the K-th largest, or the lower value lo.
+template <int kCap>
+__device__ __forceinline__ uint32_t wave_keep_top(WaveShared<kCap>& sh, int& cnt, int K,
+                                                  int slack) {
+  constexpr int SL = kCap / 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t u[SL];
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+  // each loop below takes the count through an empty asm of its own, so that no loop's
+  // per-slot validity masks are held for a later one
+  int c0 = cnt;
+  asm volatile("" : "+v"(c0));
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    u[i] = sh.u[64 * i + lane];
+    if (64 * i + lane < c0) {
+      mx = u[i] > mx ? u[i] : mx;
+      mn = u[i] < mn ? u[i] : mn;
+    }
+  }
+  mx = wave_max(mx);
+  mn = wave_min(mn);
+  uint32_t T = mn;
+  int kRem = K, inBin = 0;
+  wave_window_select<SL>(
+      [&](int i, int c, bool& valid) {
+        valid = 64 * i + lane < c;
+        return u[i];
+      },
+      cnt, sh.hist, T, mx - mn, kRem, inBin, slack);
+  // keys >= T are kept when the bin fits the slack; otherwise the bin is the single value T
+  // and of its inBin keys the kRem with the smallest ids are kept: a second select over ~id
+  uint32_t nidMin = 0u;
+  int kept = (K - kRem) + inBin;
+  if (inBin - kRem > slack) {
+    uint32_t a = 0u, z = 0xFFFFFFFFu;
+    int c2 = cnt;
+    asm volatile("" : "+v"(c2));
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      if (64 * i + lane < c2 && u[i] == T) {
+        const uint32_t nid = ~sh.id[64 * i + lane];
+        a = nid > a ? nid : a;
+        z = nid < z ? nid : z;
+      }
+    }
+    a = wave_max(a);
+    z = wave_min(z);
+    nidMin = z;
+    int kTie = kRem, inTie = 0;
+    wave_window_select<SL>(
+        [&](int i, int c, bool& valid) {
+          valid = 64 * i + lane < c && u[i] == T;
+          return ~sh.id[64 * i + lane];
+        },
+        cnt, sh.hist, nidMin, a - z, kTie, inTie, 0);
+    kept = K;
+  }
+  int pos = 0;
+  int c1 = cnt;
+  asm volatile("" : "+v"(c1));
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const uint32_t eu = sh.u[64 * i + lane], eid = sh.id[64 * i + lane];
+    const bool keep = 64 * i + lane < c1 && (eu > T || (eu == T && ~eid >= nidMin));
+    const uint64_t m = __ballot(keep);
+    // in place: the p-th kept entry moves to p <= its own index, and a slot is read before
+    // any of its entries is written
+    const int p = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos));
+    if (keep) {
+      sh.u[p] = eu;
+      sh.id[p] = eid;
+    }
+    pos += __popcll(m);
+  }
+  wave_sync();
+  cnt = kept;
+  return T;
+}
+
+// Bitonic sort, descending, of 64 * E 64-bit values held by one wave; lane l holds elements
+// e * 64 + l.  Strides below 64 by DPP moves and permlane swaps, larger ones within a lane.
+template <int E>
+__device__ __forceinline__ void sort_wave_desc(uint64_t (&v)[E]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64 * E; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int je = j / 64;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & je) continue;
+          const bool desc = ((e * 64) & k) == 0;  // k >= 128: the lane bits do not matter
+          const uint64_t x = v[e], y = v[e | je];
+          const bool sw = desc ? x < y : x > y;
+          v[e] = sw ? y : x;
+          v[e | je] = sw ? x : y;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int x = e * 64 + lane;
+          const uint64_t w = xor_lane64(v[e], j);
+          const bool keepMax = ((x & k) == 0) == ((x & j) == 0);
+          const bool wBig = w > v[e];
+          v[e] = (keepMax == wBig) ? w : v[e];
+        }
+      }
+    }
+  }
+}
+
+// KPL keys per lane of the step starting at id s: lane l takes the 16-byte groups
+// s + 4 (g * 64 + l).  kVec: one 16-byte load per group (groups past n load the row's first
+// keys); otherwise one load per key at min(id, n - 1).  Raw FP32 bits; the caller masks.
+template <int KPL, bool kVec>
+__device__ __forceinline__ void load_step(const float* row, int n, int s, uint32_t (&raw)[KPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int g = 0; g < KPL / 4; ++g) {
+    const int base = s + (g * 64 + lane) * 4;
+    if constexpr (kVec) {
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(row + (base < n ? base : 0)));
+      raw[4 * g + 0] = v.x;
+      raw[4 * g + 1] = v.y;
+      raw[4 * g + 2] = v.z;
+      raw[4 * g + 3] = v.w;
+    } else {
+      const unsigned* r32 = reinterpret_cast<const unsigned*>(row);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[4 * g + e] = __builtin_nontemporal_load(r32 + min(base + e, n - 1));
+    }
+  }
+}
+
+template <int kCap, int KPL, bool kVec>
+__global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkArgs a) {
+  constexpr int kStep = 64 * KPL;
+  constexpr int kSlack = kCap - kStep - kTopK;  // a cut during the walk leaves room for a step
+  static_assert(kCap % 256 == 0 && kSlack >= 0, "a step must fit a cut buffer");
+  __shared__ WaveShared<kCap> shAll[kWaveRows];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * kWaveRows + wave;
+  if (i >= a.numRows) return;
+  WaveShared<kCap>& sh = shAll[wave];
+  const int64_t r = a.rowStart + i, b = r / a.S, t = r % a.S;
+  int32_t* out = a.outIdx + r * kIndexWidth;
+  const int64_t c = a.ctx[b];
+  if (c <= 0 || t >= c) {
+    for (int s = lane; s < kIndexWidth; s += 64) out[s] = -1;
+    return;
+  }
+  const int64_t nVisT = (t + 1) / 4;
+  const int n = (int)(nVisT < a.numBlocks ? nVisT : a.numBlocks);
+  const int kSel = n < kTopK ? n : kTopK;
+  const float* row = a.logits + i * a.numBlocks;
+  int cnt = 0;
+  if (n > 0) {
+    // the first min(n, kCap) keys, each at its id
+    {
+      constexpr int FL = kCap / 64;
+      uint32_t raw[FL];
+      load_step<FL, kVec>(row, n, 0, raw);
+#pragma unroll
+      for (int g = 0; g < FL / 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int id = (g * 64 + lane) * 4 + e;
+          sh.u[id] = orderable_bits(raw[4 * g + e]);
+          sh.id[id] = (uint32_t)id;
+        }
+      cnt = n < kCap ? n : kCap;
+    }
+    wave_sync();
+    // The walk.  thr = 0 before the first cut: the buffer then holds kCap >= kTopK real keys
+    // with smaller ids, so a later key with u = 0 is never among the kTopK largest.  The step
+    // past the row's end makes the exact cut to kTopK.
+    uint32_t thr = 0u;
+    uint32_t cur[KPL], nxt[KPL];
+    if (n > kCap) load_step<KPL, kVec>(row, n, kCap, cur);
+    for (int s = kCap;; s += kStep) {
+      const bool more = s < n;
+      int total = 0;
+      if (more) {
+        if (s + kStep < n) load_step<KPL, kVec>(row, n, s + kStep, nxt);
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) cur[k] = orderable_bits(cur[k]);
+        if (s + kStep > n) {
+          asm volatile("");  // a branch: only the last step masks its keys past n
+#pragma unroll
+          for (int k = 0; k < KPL; ++k)
+            if (s + ((k >> 2) * 64 + lane) * 4 + (k & 3) >= n) cur[k] = 0u;  // never > thr
+        }
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
+      }
+      if (more ? cnt + total > kCap : cnt > kTopK)
+        thr = wave_keep_top<kCap>(sh, cnt, kTopK, more ? kSlack : 0);
+      if (!more) break;
+      // thr through an empty asm: the comparisons are made again rather than the counting
+      // loop's masks held across the cut
+      uint32_t th = thr;
+      asm volatile("" : "+v"(th));
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) {
+        const bool p = cur[k] > th;
+        const uint64_t m = __ballot(p);
+        // cnt + (keys of this step) <= kCap: the count above, or a cut to <= kCap - kStep
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+        if (p) {
+          sh.u[pos] = cur[k];
+          sh.id[pos] = (uint32_t)(s + ((k >> 2) * 64 + lane) * 4 + (k & 3));
+        }
+        cnt += __popcll(m);
+      }
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) cur[k] = nxt[k];
+    }
+    wave_sync();
+  }
+  // sort the cnt = kSel selected keys; padding composites are 0 and sort last
+  constexpr int E = kTopK / 64;
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 64 * e + lane;
+    v[e] = j < cnt ? composite(sh.u[j], (int)sh.id[j]) : 0ull;
+  }
+  sort_wave_desc<E>(v);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int p = 64 * e + lane;
+    if (p < kSel) {
+      const int id = (int)~(uint32_t)v[e];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[4 * p + j] = 4 * id + j;
+    }
+  }
+  const int tail = (int)((t + 1) % 4);
+  for (int s = 4 * kSel + lane; s < kIndexWidth; s += 64)
+    out[s] = s - 4 * kSel < tail ? (int)(4 * nVisT + (s - 4 * kSel)) : -1;
+}
+
 // ------------------------------------------------------------------------ streaming ---
 
 // Inclusive suffix sum over the 256 threads of the block: thread j returns sum_{i >= j} v_i.
@@ -716,76 +1081,6 @@ __device__ void radix_select(const float* keys, int n, int kSel, SelectShared& s
   }
   *thr = prefix;
   *need = kRem;
-}
-
-// Prefill selection + K4 for one row of the chunk (rows longer than the register-resident
-// kernels hold).  Candidates are the row's visible blocks [0, nVis): the entries past them
-// are -FLT_MAX by the scores contract and are not read.
-__global__ __launch_bounds__(kSelThreads) void topk_expand_stream_kernel(TopkArgs a) {
-  __shared__ SelectShared sh;
-  __shared__ uint32_t selKey[kTopK];
-  __shared__ int32_t selId[kTopK];
-  const int tid = threadIdx.x;
-  const int64_t i = blockIdx.x, r = a.rowStart + i, b = r / a.S, t = r % a.S;
-  int32_t* out = a.outIdx + r * kIndexWidth;
-  const int64_t c = a.ctx[b];
-  if (c <= 0 || t >= c) {
-    for (int s = tid; s < kIndexWidth; s += kSelThreads) out[s] = -1;
-    return;
-  }
-  const int64_t nVisT = (t + 1) / 4;
-  const int n = (int)(nVisT < a.numBlocks ? nVisT : a.numBlocks);
-  const int kSel = n < kTopK ? n : kTopK;
-  const float* keys = a.logits + i * a.numBlocks;
-  uint32_t thr = 0;
-  int need = n;  // n <= kTopK: every candidate is taken
-  if (n > kTopK) radix_select(keys, n, kSel, sh, &thr, &need);
-  // compaction in ascending id
-  int eqBefore = 0, selBefore = 0;
-  for (int base = 0; base < n; base += kSelThreads) {
-    const int g = base + tid;
-    const uint32_t u = g < n ? orderable(keys[g]) : 0u;
-    const bool eq = g < n && (n <= kTopK || u == thr);
-    int eqTot, selTot;
-    const int eqRank = block_rank(eq, sh.wave, &eqTot) + eqBefore;
-    const bool sel = g < n && (n <= kTopK || u > thr || (eq && eqRank < need));
-    const int pos = block_rank(sel, sh.wave, &selTot) + selBefore;
-    if (sel && pos < kTopK) {
-      selKey[pos] = u;
-      selId[pos] = g;
-    }
-    eqBefore += eqTot;
-    selBefore += selTot;
-  }
-  // pad to 512 with entries that sort last, then bitonic sort: key descending, id ascending
-  for (int s = kSel + tid; s < kTopK; s += kSelThreads) {
-    selKey[s] = 0u;
-    selId[s] = 0x7FFFFFFF;
-  }
-  __syncthreads();
-  for (int size = 2; size <= kTopK; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int x = tid; x < kTopK; x += kSelThreads) {
-        const int y = x ^ stride;
-        if (y > x) {
-          const bool descBlock = (x & size) == 0;  // this half of the network sorts "first"
-          const uint32_t kx = selKey[x], ky = selKey[y];
-          const int32_t ix = selId[x], iy = selId[y];
-          // "first" = larger key, then smaller id
-          const bool yFirst = ky > kx || (ky == kx && iy < ix);
-          if (yFirst == descBlock) {
-            selKey[x] = ky;
-            selKey[y] = kx;
-            selId[x] = iy;
-            selId[y] = ix;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int s = tid; s < 4 * kSel; s += kSelThreads) out[s] = selId[s >> 2] * 4 + (s & 3);
-  write_tail_and_pad(out, 4 * kSel, nVisT, (int)((t + 1) % 4), kSelThreads);
 }
 
 // Decode selection + expand for one sequence (rows longer than the register-resident kernels
@@ -898,8 +1193,14 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   const bool aligned = (a.numBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   const int kpt = keys_per_thread(nMax, kRT);
   const dim3 grid((unsigned)a.numRows);
-  if (kpt == 0) {
-    hipLaunchKernelGGL(topk_expand_stream_kernel, grid, dim3(kSelThreads), 0, stream, a);
+  if (kpt == 0) {  // rows longer than the register-resident kernel holds
+    const dim3 wgrid((unsigned)((a.numRows + kWaveRows - 1) / kWaveRows));
+    if (aligned)
+      hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCap, kWaveKPL, true>), wgrid,
+                         dim3(64 * kWaveRows), 0, stream, a);
+    else
+      hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCap, kWaveKPL, false>), wgrid,
+                         dim3(64 * kWaveRows), 0, stream, a);
   } else {
     switch (kpt) {
       QSA_REG_CASE(topk_expand_reg_kernel, 4, kRT, grid, a)

@@ -98,8 +98,19 @@ LONG_CASES = {
     "mid": (1, 40000, 10000, [40000], 20000, 64, ("scores", "normal", "ties", "special_ge")),
     # a chunk across two sequences: short rows of sequence 1 beside long rows of sequence 0
     "cross": (2, 12000, 3000, [12000, 11000], 11990, 30, ("scores", "normal")),
-    # rows longer than the register-resident kernels hold (streaming kernel)
+    # rows longer than 32768 blocks (one wave per row, candidate buffer in LDS)
     "stream": (1, 140000, 35000, [140000], 140000 - 6, 6, ("scores", "normal", "ties")),
+    # the same kernel on numBlocks not a multiple of 4: four rows of 32768-32771 blocks beside
+    # every length from 0 to 1537 blocks of a second sequence (one candidate buffer holds
+    # 1536), and its padded rows
+    "long_unaligned": (2, 131080, 32771, [131080, 6150], 131080 - 4, 4 + 6200,
+                       ("scores", "ties", "normal", "special_ge")),
+    # numBlocks not a multiple of 4 (one load per key): eight rows of 2249-2251 blocks beside
+    # every length from 0 to 1750 blocks of a second sequence, and its padded rows
+    "unaligned": (2, 9004, 2251, [9004, 7000], 9004 - 8, 8 + 7100,
+                  ("scores", "ties", "normal", "special_ge")),
+    # rows of 2045 to 2050 blocks: around one full candidate buffer of the long-row kernel
+    "buffer_edge": (1, 8200, 2100, [8200], 8180, 20, ("scores", "ties", "normal")),
 }
 
 
@@ -132,8 +143,8 @@ def _run_long(qsa, O, B, S, nb, ctx, r0, n, logits, what):
 
 @pytest.mark.parametrize("case", list(LONG_CASES))
 def test_topk_expand_long_rows(qsa, O, case):
-    """Rows of 3000 to 35000 complete blocks: every register width of the register-resident
-    kernel up to 64 keys per thread, a chunk across two sequences, and the streaming kernel past
+    """Rows of up to 35000 complete blocks: chunks across two sequences (long rows beside short
+    and padded ones), numBlocks not a multiple of 4, rows around one candidate buffer and past
     32768 blocks; value styles with recurring values, many ties at the threshold (all equal
     included), +-0, +-inf, NaN and -FLT_MAX."""
     _run_long(qsa, O, *_long_case(case), case)
