@@ -255,23 +255,12 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int64_t b = blockIdx.x;
-  const int64_t ctx = a.ctx[b];
-  int64_t nVis = ctx > 0 ? ctx / 4 : 0;
-  if (nVis > a.maxBlocks) nVis = a.maxBlocks;
   const int64_t gBase = kDecBlocks * (int64_t)blockIdx.y;
-  if (gBase >= nVis) return;
-  float qa[4][4], qb[4][4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const Piece p = load_piece(a.qNormed, (b * 4 + h) * kDim, c);
-    widen4(T{}, p.a, qa[h]);
-    widen4(T{}, p.b, qb[h]);
-  }
-  const float scale = score_scale();
-  // the row's kDecK blocks: all page-table entries first, then all V-tail rows, then the dots, so
-  // the two dependent memory latencies are paid once rather than once per block
-  // (the page table is read at a clamped slot unconditionally; the guards of tail_offset -- slot
-  // in range, entry not -1 and inside the pool -- are applied afterwards)
+  // The page-table entries of the row's kDecK blocks and the sequence's q depend on the block
+  // index alone: they are loaded before the context length is known, and the V-tail addresses
+  // depend on the entries alone (a block past the context, or behind an entry that fails a
+  // guard of tail_offset -- slot in range, entry not -1 and inside the pool -- reads page 0's
+  // row, unused), so the dependent latencies are the entry's and the V-tail's.
   const int32_t* vt = a.pool.pageTable + (b * 2 + 1) * a.pool.maxPagesPerSeq;
   int32_t id[kDecK];
 #pragma unroll
@@ -279,24 +268,40 @@ __global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArg
     const int64_t slot = (4 * (gBase + 4 * wave + r + 16 * k)) >> 7;
     id[k] = vt[slot < a.pool.maxPagesPerSeq ? slot : a.pool.maxPagesPerSeq - 1];
   }
+  Piece qp[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) qp[h] = load_piece(a.qNormed, (b * 4 + h) * kDim, c);
+  // a memory clobber: the loads above are issued here, not sunk past the early return below
+  asm volatile("" ::: "memory");
+  const int64_t ctx = a.ctx[b];
+  int64_t nVis = ctx > 0 ? ctx / 4 : 0;
+  if (nVis > a.maxBlocks) nVis = a.maxBlocks;
+  if (gBase >= nVis) return;
   int64_t off[kDecK];
+  bool okT[kDecK];
 #pragma unroll
   for (int k = 0; k < kDecK; ++k) {
     const int64_t g = gBase + 4 * wave + r + 16 * k, pos = 4 * g;
-    const bool ok = g < nVis && (pos >> 7) < a.pool.maxPagesPerSeq && id[k] >= 0 &&
-                    id[k] < a.pool.numIds;
-    off[k] = ok ? ((int64_t)id[k] * kPageTokens + (pos & (kPageTokens - 1))) * a.pool.rowElems +
-                      a.pool.headSize
-                : -1;
+    okT[k] = ((pos >> 7) < a.pool.maxPagesPerSeq) & (id[k] >= 0) & (id[k] < a.pool.numIds);
+    const int64_t o = ((int64_t)(okT[k] ? id[k] : 0) * kPageTokens + (pos & (kPageTokens - 1))) *
+                          a.pool.rowElems + a.pool.headSize;
+    off[k] = okT[k] ? o : 0;
   }
-  Piece kp[kDecK];  // unconditional loads (a skipped block reads page 0's row, unused)
+  Piece kp[kDecK];
 #pragma unroll
-  for (int k = 0; k < kDecK; ++k) kp[k] = load_piece(a.pool.base, off[k] >= 0 ? off[k] : 0, c);
+  for (int k = 0; k < kDecK; ++k) kp[k] = load_piece(a.pool.base, off[k], c);
+  float qa[4][4], qb[4][4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    widen4(T{}, qp[h].a, qa[h]);
+    widen4(T{}, qp[h].b, qb[h]);
+  }
+  const float scale = score_scale();
 #pragma unroll
   for (int k = 0; k < kDecK; ++k) {
     const int64_t g = gBase + 4 * wave + r + 16 * k;
     if (g >= nVis) break;
-    if (off[k] < 0) {  // unused or out-of-range V page entry
+    if (!okT[k]) {  // unused or out-of-range V page entry
       if (c == 0) a.logits[b * a.maxBlocks + g] = -FLT_MAX;
       continue;
     }

@@ -181,7 +181,8 @@ def test_scores_narrow_numblocks(qsa, O):
 def test_scores_decode(qsa, O, dt):
     """Decode scores of one query token per sequence against V-tails that the oracle's K1b
     wrote into a host pool (the same pool bits are uploaded for the GPU call); entries past
-    each row's prefix keep their content; an unused V page entry scores -FLT_MAX."""
+    each row's prefix keep their content; an unused V page entry, and one past the pool, score
+    -FLT_MAX."""
     rng = np.random.default_rng(101)
     L = np.array([4000, 1031, 7, 3, 2048, 513, 0, 64], np.int32)
     B, Lmax = len(L), int(L.max())
@@ -192,6 +193,7 @@ def test_scores_decode(qsa, O, dt):
     pt = np.stack([rng.permutation(numPages)[:B * m].reshape(B, m),
                    rng.permutation(numPages)[:B * m].reshape(B, m) + numPages], 1).astype(np.int32)
     pt[1, 1, 3] = -1
+    pt[0, 1, 5] = 2 * numPages                  # past the pool: not a V page
     spec = W.PoolSpec(numPages, pt)
     cs = W.cos_sin_table(Lmax + 8, 1e4)
     nb = (Lmax + 3) // 4
@@ -213,6 +215,7 @@ def test_scores_decode(qsa, O, dt):
             "hd,gd->g", np.abs(G.widen(qdec[b, 0], dt)), np.abs(G.widen(kbh[b, :n], dt)))
         check_logits(got[b, :n], ref[b, :n], bound, f"decode seq {b}")
     assert np.all(got[1, 96:128] == NEG)
+    assert np.all(got[0, 160:192] == NEG)
 
 
 def test_scores_decode_bench_batch(qsa, O):
