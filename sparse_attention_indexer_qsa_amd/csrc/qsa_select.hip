@@ -642,11 +642,11 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
 
 // -------------------------------------------------------------------- one wave per row ---
 //
-// Prefill rows longer than 32768 blocks.  Each wave of a workgroup takes a row of its own and walks it
-// front to back, a step of keys at a time, against a running threshold thr: a wave-private
-// LDS buffer holds candidates {u, id}; whenever the next step's keys above thr would not fit,
-// the buffer is cut to a few more than its 512 largest (u desc, id asc), all of them at or
-// above some value lo, and thr becomes lo.  Later keys have larger ids, so one of them can be
+// Prefill rows longer than 32768 blocks.  Each wave of a workgroup takes a row of its own and
+// walks it front to back, a step of keys at a time, against a running threshold thr: a
+// wave-private LDS buffer holds candidates {u, id}; whenever the next step's keys above thr
+// would not fit, the buffer is cut to its 512 largest (u desc, id asc) and at most kCap - 512
+// - (one step) more, all of them at or above some value lo, and thr becomes lo.  Later keys have larger ids, so one of them can be
 // among a prefix's 512 largest only if u > thr: equal u loses the tie.  The buffer therefore
 // always holds the 512 largest keys seen so far; at the end it is cut to exactly those 512,
 // which are sorted in registers.  No workgroup barrier: the waves of a workgroup share
