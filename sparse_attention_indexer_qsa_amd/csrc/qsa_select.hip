@@ -16,10 +16,12 @@
 //  * Padding: registers past the row hold u = 0 with ids >= n.  In the (u desc, id asc)
 //    order every padding key comes after every real key, so while kSel <= n the kSel first
 //    keys of the padded row are those of the row, and no step needs to tell them apart.
-//  * Window: once n >= 2048 the even and the odd register groups of every thread hold real
-//    keys, and the smallest of those 512 maxima, lo, has at least 512 keys at or above it
-//    (shorter rows take lo = the row minimum); with hi the row maximum, the kSel-th largest
-//    key lies in [lo, hi].
+//  * Window: lo is the smallest of the maxima of 512 disjoint key sets that each hold a real
+//    key, so at least 512 keys are at or above it: the even and the odd register groups of
+//    each of 256 threads once n >= 2048 (prefill), each pair of the 1024 threads once
+//    n >= 4096 (decode); shorter rows take lo = the row minimum.  With hi the row maximum, the
+//    kSel-th largest key lies in [lo, hi], and rows with many equal low keys (a ReLU's zeros)
+//    keep them out of the histograms.
 //  * Radix select inside the window, MSB first: each pass histograms (LDS atomics, 256 bins)
 //    only the keys inside the current window, at a shift that spreads the window over the 256
 //    bins, and a one-wave suffix scan picks the bin holding the kSel-th largest.  The window
@@ -306,10 +308,13 @@ template <int NT, int KPT>
 __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n, int kSel,
                                                      RegShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // window [lo, hi]: at least kSel keys are >= lo.  Each thread keeps the maxima of its even
-  // and of its odd register groups; from n = 8 * NT on, both halves of every thread hold
-  // real keys and lo, the smallest of these 2 * NT >= 512 maxima, has a distinct key at or
-  // above it for each of them.  Below that, lo is the smallest real key.
+  // window [lo, hi]: at least kSel keys are >= lo.  lo is the smallest of the maxima of 512
+  // disjoint sets of keys each holding a real key, so each set has a distinct real key at or
+  // above it (padding keys are 0, below or equal to any real key).  The fewer the sets, the
+  // larger they are and the higher lo: 1024 threads form 512 pairs of threads, every thread
+  // holding a real key from n = 4 * NT on; 256 threads split each thread's register groups
+  // into even and odd, both holding real keys from n = 8 * NT on.  Below that, lo is the
+  // smallest real key.
   uint32_t mA = 0u, mB = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
@@ -318,7 +323,12 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   }
   uint32_t tmax = mA > mB ? mA : mB;
   uint32_t tmin = mA < mB ? mA : mB;
-  if (n < 8 * NT) {
+  static_assert(NT == 1024 || NT == 256, "512 sets: pairs of 1024 threads or halves of 256");
+  if constexpr (NT == 1024) {
+    const uint32_t o = __shfl_xor(tmax, 1);
+    tmin = o > tmax ? o : tmax;  // the pair's maximum
+  }
+  if (n < (NT == 1024 ? 4 : 8) * NT) {
     tmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
