@@ -100,6 +100,10 @@ LONG_CASES = {
     "cross": (2, 12000, 3000, [12000, 11000], 11990, 30, ("scores", "normal")),
     # rows longer than 32768 blocks (one wave per row, candidate buffer in LDS)
     "stream": (1, 140000, 35000, [140000], 140000 - 6, 6, ("scores", "normal", "ties")),
+    # rows of about 70000 blocks: several cuts of the candidate buffer per row, with all keys
+    # equal ("zeros") and with few distinct values, so that ties straddle every cut
+    "very_long": (1, 280000, 70000, [280000], 280000 - 5, 5,
+                  ("scores", "ties", "normal", "special_ge", "zeros")),
     # the same kernel on numBlocks not a multiple of 4: four rows of 32768-32771 blocks beside
     # every length from 0 to 1537 blocks of a second sequence (one candidate buffer holds
     # 1536), and its padded rows
