@@ -663,8 +663,8 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
 // nothing, and several rows per CU overlap their loads with the others' selection.
 
 constexpr int kWaveRows = 4;       // rows (waves) per workgroup of the one-wave-per-row kernel
-constexpr int kWaveCap = 1536;     // candidate buffer entries per row (12 rows per CU)
-constexpr int kWaveKPL = 8;        // keys per lane per step (512 keys)
+constexpr int kWaveCap = 2048;     // candidate buffer entries per row (8 rows per CU)
+constexpr int kWaveKPL = 16;       // keys per lane per step (1024 keys)
 
 template <int kCap>
 struct WaveShared {

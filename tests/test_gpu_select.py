@@ -105,9 +105,9 @@ LONG_CASES = {
     "very_long": (1, 280000, 70000, [280000], 280000 - 5, 5,
                   ("scores", "ties", "normal", "special_ge", "zeros")),
     # the same kernel on numBlocks not a multiple of 4: four rows of 32768-32771 blocks beside
-    # every length from 0 to 1537 blocks of a second sequence (one candidate buffer holds
-    # 1536), and its padded rows
-    "long_unaligned": (2, 131080, 32771, [131080, 6150], 131080 - 4, 4 + 6200,
+    # every length from 0 to 2049 blocks of a second sequence (one candidate buffer holds
+    # 2048), and its padded rows
+    "long_unaligned": (2, 131080, 32771, [131080, 8196], 131080 - 4, 4 + 8250,
                        ("scores", "ties", "normal", "special_ge")),
     # numBlocks not a multiple of 4 (one load per key): eight rows of 2249-2251 blocks beside
     # every length from 0 to 1750 blocks of a second sequence, and its padded rows
