@@ -947,47 +947,58 @@ __global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkAr
     // The walk.  thr = 0 before the first cut: the buffer then holds kCap >= kTopK real keys
     // with smaller ids, so a later key with u = 0 is never among the kTopK largest.  The step
     // past the row's end makes the exact cut to kTopK.
+    // Two register buffers take turns (the loop is unrolled by two, so no buffer is copied):
+    // the next step's loads are in flight while a step is filtered.  They are unconditional
+    // (past n: loads of the row's start, unused): behind a branch, the wait for a step's keys
+    // at the join would also wait for the next step's loads.
     uint32_t thr = 0u;
-    uint32_t cur[KPL], nxt[KPL];
-    if (n > kCap) load_step<KPL, kVec>(row, n, kCap, cur);
-    for (int s = kCap;; s += kStep) {
-      const bool more = s < n;
-      int total = 0;
-      if (more) {
-        if (s + kStep < n) load_step<KPL, kVec>(row, n, s + kStep, nxt);
+    uint32_t ring[2][KPL];
+    load_step<KPL, kVec>(row, n, kCap, ring[0]);
+    bool done = false;
+    for (int s0 = kCap; !done; s0 += 2 * kStep) {
 #pragma unroll
-        for (int k = 0; k < KPL; ++k) cur[k] = orderable_bits(cur[k]);
-        if (s + kStep > n) {
-          asm volatile("");  // a branch: only the last step masks its keys past n
+      for (int d = 0; d < 2; ++d) {
+        const int s = s0 + d * kStep;
+        load_step<KPL, kVec>(row, n, s + kStep, ring[d ^ 1]);
+        uint32_t (&cur)[KPL] = ring[d];
+        const bool more = s < n;
+        int total = 0;
+        if (more) {
 #pragma unroll
-          for (int k = 0; k < KPL; ++k)
-            if (s + ((k >> 2) * 64 + lane) * 4 + (k & 3) >= n) cur[k] = 0u;  // never > thr
+          for (int k = 0; k < KPL; ++k) cur[k] = orderable_bits(cur[k]);
+          if (s + kStep > n) {
+            asm volatile("");  // a branch: only the last step masks its keys past n
+#pragma unroll
+            for (int k = 0; k < KPL; ++k)
+              if (s + ((k >> 2) * 64 + lane) * 4 + (k & 3) >= n) cur[k] = 0u;  // never > thr
+          }
+#pragma unroll
+          for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
         }
-#pragma unroll
-        for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
-      }
-      if (more ? cnt + total > kCap : cnt > kTopK)
-        thr = wave_keep_top<kCap>(sh, cnt, kTopK, more ? kSlack : 0);
-      if (!more) break;
-      // thr through an empty asm: the comparisons are made again rather than the counting
-      // loop's masks held across the cut
-      uint32_t th = thr;
-      asm volatile("" : "+v"(th));
-#pragma unroll
-      for (int k = 0; k < KPL; ++k) {
-        const bool p = cur[k] > th;
-        const uint64_t m = __ballot(p);
-        // cnt + (keys of this step) <= kCap: the count above, or a cut to <= kCap - kStep
-        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
-        if (p) {
-          sh.u[pos] = cur[k];
-          sh.id[pos] = (uint32_t)(s + ((k >> 2) * 64 + lane) * 4 + (k & 3));
+        if (more ? cnt + total > kCap : cnt > kTopK)
+          thr = wave_keep_top<kCap>(sh, cnt, kTopK, more ? kSlack : 0);
+        if (!more) {
+          done = true;
+          break;
         }
-        cnt += __popcll(m);
-      }
+        // thr through an empty asm: the comparisons are made again rather than the counting
+        // loop's masks held across the cut
+        uint32_t th = thr;
+        asm volatile("" : "+v"(th));
 #pragma unroll
-      for (int k = 0; k < KPL; ++k) cur[k] = nxt[k];
+        for (int k = 0; k < KPL; ++k) {
+          const bool p = cur[k] > th;
+          const uint64_t m = __ballot(p);
+          // cnt + (keys of this step) <= kCap: the count above, or a cut to <= kCap - kStep
+          const int pos = (int)__builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+          if (p) {
+            sh.u[pos] = cur[k];
+            sh.id[pos] = (uint32_t)(s + ((k >> 2) * 64 + lane) * 4 + (k & 3));
+          }
+          cnt += __popcll(m);
+        }
+      }
     }
     wave_sync();
   }
