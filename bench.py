@@ -217,6 +217,35 @@ def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=SCORE_ROWS[0]):
             "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS}
 
 
+def select_long_leg(qsa, torch, steps, warmup):
+    """Top-512 selection + expand on rows longer than 32768 blocks (one wave per row, an LDS
+    candidate buffer): the last 2048 rows of a 262144-token sequence, 65024 to 65536 complete
+    blocks each, scores-like logits (a ReLU's share of zeros, quantised so that values recur;
+    -FLT_MAX past each row's complete blocks, as the scores call writes them)."""
+    S, nb, numRows = 262144, 65536, 2048
+    rowStart = S - numRows
+    g = torch.Generator(device="cuda").manual_seed(7)
+    logits = torch.randn(numRows, nb, generator=g, device="cuda")
+    logits = torch.round(torch.relu(logits * 2.0) * 64.0) / 64.0
+    nvis = (torch.arange(rowStart, S, device="cuda") + 1) // 4
+    cols = torch.arange(nb, device="cuda")
+    logits[cols[None, :] >= nvis[:, None]] = -3.4028234663852886e38
+    out = torch.empty(S, qsa.INDEX_WIDTH, dtype=torch.int32, device="cuda")
+    ctx = torch.tensor([S], dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def call(st):
+        rc = qsa.lib.qsa_index_topk_expand(out.data_ptr(), logits.data_ptr(), ctx.data_ptr(), 1,
+                                           S, nb, rowStart, numRows, st)
+        assert rc == 0, qsa.qsa_last_error()
+    us = _time_stream(torch, call, steps, warmup)
+    alg = select_alg(S, nb, rowStart, numRows)
+    del out, logits
+    return {"workload": f"rows [{rowStart}, {S}) of a {S}-token sequence x {nb} blocks",
+            "entry": "qsa_index_topk_expand", "us_per_call": us, "alg_bytes": alg,
+            "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS}
+
+
 def scores_decode_leg(qsa, torch, steps, warmup):
     """Decode block scores (qsa_index_scores_decode) for the decode workload's 64 sequences,
     one new token each (contexts up to 32772): kbar gathered from the V-tails of the paged
@@ -611,7 +640,7 @@ def main():
             torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
 
-    scores = select = select_decode = scores_decode = None
+    scores = select = select_long = select_decode = scores_decode = None
     if not args.no_scores:
         print("[bench] timing the block scores", file=sys.stderr, flush=True)
         logits, scores = scores_leg(qsa, torch, sets[0], wl, min(args.steps, 50),
@@ -619,6 +648,9 @@ def main():
         print("[bench] timing the top-512 selection", file=sys.stderr, flush=True)
         select = select_leg(qsa, torch, wl, logits, min(args.steps, 50), min(args.warmup, 5))
         del logits
+        print("[bench] timing the selection on rows past 32768 blocks", file=sys.stderr,
+              flush=True)
+        select_long = select_long_leg(qsa, torch, min(args.steps, 50), min(args.warmup, 5))
         select_decode = select_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
         scores_decode = scores_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
     decode = None
@@ -657,6 +689,7 @@ def main():
         "decode_pre_pass": decode,
         "scores": scores,
         "select": select,
+        "select_long_rows": select_long,
         "scores_decode": scores_decode,
         "select_decode": select_decode,
     }
