@@ -225,8 +225,10 @@ def select_long_leg(qsa, torch, steps, warmup):
     S, nb, numRows = 262144, 65536, 2048
     rowStart = S - numRows
     g = torch.Generator(device="cuda").manual_seed(7)
+    # relu(2 x) quantised to 1/64, by divisions only: a multiply would launch the kernel the
+    # counter calibration identifies as its reference (torch.mul, --copy-calib)
     logits = torch.randn(numRows, nb, generator=g, device="cuda")
-    logits = torch.round(torch.relu(logits * 2.0) * 64.0) / 64.0
+    logits = torch.round(torch.relu(logits) / 0.0078125) / 64.0
     nvis = (torch.arange(rowStart, S, device="cuda") + 1) // 4
     cols = torch.arange(nb, device="cuda")
     logits[cols[None, :] >= nvis[:, None]] = -3.4028234663852886e38
@@ -422,7 +424,8 @@ def summarize(trace_dir, fetch_dir, write_dir):
         assert ks, (key, list(d))
         return d[ks[0]][0]
 
-    copy_key = "MulFunctor"   # torch.mul over 256 MiB of float32 (--copy-calib)
+    copy_key = "MulFunctor"   # torch.mul over 256 MiB of float32 (--copy-calib); no other
+    #                           leg of a counter run may launch a float multiply
     f_copy, w_copy = pick(fetch, copy_key), pick(write, copy_key)
     f_scale, w_scale = COPY_BYTES / (f_copy * 1024), COPY_BYTES / (w_copy * 1024)
     f_k, w_k = pick(fetch, "prefill_kernel"), pick(write, "prefill_kernel")
@@ -481,9 +484,12 @@ def summarize_next(stats, fetch, write, f_scale, w_scale):
     legs = [("scores_kernel", "`scores_kernel<Bf16>` (qsa_index_scores)",
              scores_alg(S, nb, r0, nr)[0]),
             ("topk_expand_reg_kernel", "`topk_expand_reg_kernel` (qsa_index_topk_expand)",
-             select_alg(S, nb, r0, nr))]
+             select_alg(S, nb, r0, nr)),
+            ("topk_expand_wave_kernel", "`topk_expand_wave_kernel` (qsa_index_topk_expand; "
+             "rows [260096, 262144) of a 262144-token sequence x 65536 blocks)",
+             select_alg(262144, 65536, 262144 - 2048, 2048))]
     md = ["# Block scores and top-512 selection — long prefill rows [65536, 73728) x 32768 "
-          "blocks, bf16", "",
+          "blocks, bf16 (and the selection on rows past 32768 blocks)", "",
           "MI355X (gfx950), one GPU.  Kernel durations from the trace, HBM bytes from the "
           "counter runs of `prefill_kernel_long_prefill.md` (same commands, same scale factors "
           f"x {f_scale:.3f} for FETCH_SIZE and x {w_scale:.3f} for WRITE_SIZE).", "",
