@@ -301,7 +301,7 @@ int qsa_index_topk_expand(int32_t* outIdx, const float* logits, const int32_t* c
  * tokens then start at 4*maxBlocks); tail = ctx % 4.  nVis <= 512 takes every block 0..nVis-1
  * and reads no logits.  Otherwise the kSel = 512 largest keys of [0, nVis), equal keys at the
  * threshold in ascending id, emitted in ascending block id.  ctx <= 0 gives an all -1 row.
- * One 1024-thread workgroup per sequence: batchSize <= 2^22 - 1, else QSA_E_INVALID.
+ * One 512-thread workgroup per sequence: batchSize <= 2^23 - 1, else QSA_E_INVALID.
  */
 int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits,
                                  const int32_t* contextLengths, int32_t* splitCounters,

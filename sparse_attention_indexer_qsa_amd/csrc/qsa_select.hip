@@ -9,8 +9,8 @@
 // Keys are the monotone map of the FP32 bits, u = bits >= 0 ? bits | 0x80000000 : ~bits; a
 // row's order is descending u, equal u in ascending block id (the stable sort's order).
 //
-// Register-resident rows (prefill: 256 threads, up to 128 keys each; decode: 1024 threads per
-// sequence, up to 32 keys each, which shortens a sequence's latency; 32768 blocks at most):
+// Register-resident rows (prefill: 256 threads, up to 128 keys each; decode: 512 threads per
+// sequence, up to 64 keys each, which shortens a sequence's latency; 32768 blocks at most):
 //  * The row is read from HBM once, 16 bytes per lane, into registers.  Thread t holds the
 //    ids ((g * threads + t) * 4 + e) for its register groups g and e < 4.
 //  * Padding: registers past the row hold u = 0 with ids >= n.  In the (u desc, id asc)
@@ -18,8 +18,8 @@
 //    keys of the padded row are those of the row, and no step needs to tell them apart.
 //  * Window: lo is the smallest of the maxima of 512 disjoint key sets that each hold a real
 //    key, so at least 512 keys are at or above it: the even and the odd register groups of
-//    each of 256 threads once n >= 2048 (prefill), each pair of the 1024 threads once
-//    n >= 4096 (decode); shorter rows take lo = the row minimum.  With hi the row maximum, the
+//    each of 256 threads once n >= 2048 (prefill), all the keys of each of 512 threads once
+//    n >= 2048 (decode); shorter rows take lo = the row minimum.  With hi the row maximum, the
 //    kSel-th largest key lies in [lo, hi], and rows with many equal low keys (a ReLU's zeros)
 //    keep them out of the histograms.
 //  * Radix select inside the window, MSB first: each pass histograms (LDS atomics, 256 bins)
@@ -55,7 +55,7 @@ constexpr int kTopK = 512;
 constexpr int kIndexWidth = 2051;   // 4 * 512 + 3
 constexpr int kSelThreads = 256;    // streaming kernels
 constexpr int kRT = 256;            // register-resident prefill kernel: threads per row
-constexpr int kDT = 1024;           // register-resident decode kernel: threads per sequence
+constexpr int kDT = 512;            // register-resident decode kernel: threads per sequence
 constexpr int kMaxW = kDT / 64;     // most waves of a register-resident workgroup
 constexpr int kCandCap = 2048;      // keys kept in LDS after the first radix pass
 
@@ -311,10 +311,10 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   // window [lo, hi]: at least kSel keys are >= lo.  lo is the smallest of the maxima of 512
   // disjoint sets of keys each holding a real key, so each set has a distinct real key at or
   // above it (padding keys are 0, below or equal to any real key).  The fewer the sets, the
-  // larger they are and the higher lo: 1024 threads form 512 pairs of threads, every thread
-  // holding a real key from n = 4 * NT on; 256 threads split each thread's register groups
-  // into even and odd, both holding real keys from n = 8 * NT on.  Below that, lo is the
-  // smallest real key.
+  // larger they are and the higher lo: 512 threads each form one set, every thread holding a
+  // real key from n = 4 * NT on; 256 threads split each thread's register groups into even
+  // and odd, both holding real keys from n = 8 * NT on.  Below that, lo is the smallest real
+  // key.
   uint32_t mA = 0u, mB = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
@@ -323,12 +323,9 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   }
   uint32_t tmax = mA > mB ? mA : mB;
   uint32_t tmin = mA < mB ? mA : mB;
-  static_assert(NT == 1024 || NT == 256, "512 sets: pairs of 1024 threads or halves of 256");
-  if constexpr (NT == 1024) {
-    const uint32_t o = __shfl_xor(tmax, 1);
-    tmin = o > tmax ? o : tmax;  // the pair's maximum
-  }
-  if (n < (NT == 1024 ? 4 : 8) * NT) {
+  static_assert(NT == 512 || NT == 256, "512 sets: threads of 512 or halves of 256");
+  if constexpr (NT == 512) tmin = tmax;  // the thread's maximum
+  if (n < (NT == 512 ? 4 : 8) * NT) {
     tmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
@@ -1251,7 +1248,9 @@ hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream
       QSA_REG_CASE(topk_expand_decode_reg_kernel, 8, kDT, grid, a)
       QSA_REG_CASE(topk_expand_decode_reg_kernel, 16, kDT, grid, a)
       QSA_REG_CASE(topk_expand_decode_reg_kernel, 24, kDT, grid, a)
-      default: QSA_REG_CASE(topk_expand_decode_reg_kernel, 32, kDT, grid, a)
+      QSA_REG_CASE(topk_expand_decode_reg_kernel, 32, kDT, grid, a)
+      QSA_REG_CASE(topk_expand_decode_reg_kernel, 48, kDT, grid, a)
+      default: QSA_REG_CASE(topk_expand_decode_reg_kernel, 64, kDT, grid, a)
     }
   }
   return hipGetLastError();

@@ -267,7 +267,7 @@ def test_next_rows_validation(qsa, host):
                                               a["B"], a["mb"], None)
     assert tkd(B=-1) == E and tkd(mb=-1) == E and tkd(sc=h.p(4), H=-1) == E
     assert tkd(sc=h.p(4, 2), H=2) == A and tkd(out=None) == E and tkd(lg=None) == E
-    assert tkd(B=2**22) == E                                  # 1024-thread workgroups
+    assert tkd(B=2**23) == E                                  # 512-thread workgroups
     assert tkd(mb=512, lg=None) != E                          # nVis <= 512 reads no logits
     assert tkd(B=0, out=None) == OK
 
