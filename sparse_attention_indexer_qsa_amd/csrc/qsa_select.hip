@@ -9,8 +9,9 @@
 // Keys are the monotone map of the FP32 bits, u = bits >= 0 ? bits | 0x80000000 : ~bits; a
 // row's order is descending u, equal u in ascending block id (the stable sort's order).
 //
-// Register-resident rows (prefill: 256 threads, up to 128 keys each; decode: 512 threads per
-// sequence, up to 64 keys each, which shortens a sequence's latency; 32768 blocks at most):
+// Register-resident rows (prefill: 256 threads, up to 72 keys each, 18432 blocks at most;
+// decode: 512 threads per sequence, up to 64 keys each, which shortens a sequence's latency,
+// 32768 blocks at most):
 //  * The row is read from HBM once, 16 bytes per lane, into registers.  Thread t holds the
 //    ids ((g * threads + t) * 4 + e) for its register groups g and e < 4.
 //  * Padding: registers past the row hold u = 0 with ids >= n.  In the (u desc, id asc)
@@ -39,7 +40,7 @@
 //  * Decode: the selection is emitted in ascending id: one block scan per register group
 //    counts, for each key, the keys above T and the keys equal to T with smaller ids.
 //
-// Prefill rows longer than 32768 blocks take the one-wave-per-row kernel (a walk of the row
+// Prefill rows longer than 18432 blocks take the one-wave-per-row kernel (a walk of the row
 // against a running threshold into an LDS candidate buffer, below).  Decode rows that long
 // take the streaming kernel at the end of the file (the same radix select with 8-bit digits
 // over the whole key range, the row re-read from L2 on every pass), 256 threads per row.
@@ -58,6 +59,7 @@ constexpr int kRT = 256;            // register-resident prefill kernel: threads
 constexpr int kDT = 512;            // register-resident decode kernel: threads per sequence
 constexpr int kMaxW = kDT / 64;     // most waves of a register-resident workgroup
 constexpr int kCandCap = 2048;      // keys kept in LDS after the first radix pass
+constexpr int kRegMaxKeys = 72;     // prefill: most keys per thread of the register kernel
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -649,7 +651,7 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
 
 // -------------------------------------------------------------------- one wave per row ---
 //
-// Prefill rows longer than 32768 blocks.  Each wave of a workgroup takes a row of its own and
+// Prefill rows longer than 18432 blocks.  Each wave of a workgroup takes a row of its own and
 // walks it front to back, a step of keys at a time, against a running threshold thr: a
 // wave-private LDS buffer holds candidates {u, id}; whenever the next step's keys above thr
 // would not fit, the buffer is cut to its 512 largest (u desc, id asc) and at most kCap - 512
@@ -1211,7 +1213,10 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   const bool aligned = (a.numBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   const int kpt = keys_per_thread(nMax, kRT);
   const dim3 grid((unsigned)a.numRows);
-  if (kpt == 0) {  // rows longer than the register-resident kernel holds
+  // past 72 keys per thread the register kernel holds fewer than 4 rows per CU and the
+  // one-wave-per-row kernel is faster (rows of 18500 blocks: 129 against 145 us per 4096 rows;
+  // 32768 blocks: 176 against 224 us)
+  if (kpt == 0 || kpt > kRegMaxKeys) {
     const dim3 wgrid((unsigned)((a.numRows + kWaveRows - 1) / kWaveRows));
     if (aligned)
       hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCap, kWaveKPL, true>), wgrid,
@@ -1228,9 +1233,7 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
       QSA_REG_CASE(topk_expand_reg_kernel, 32, kRT, grid, a)
       QSA_REG_CASE(topk_expand_reg_kernel, 48, kRT, grid, a)
       QSA_REG_CASE(topk_expand_reg_kernel, 64, kRT, grid, a)
-      QSA_REG_CASE(topk_expand_reg_kernel, 72, kRT, grid, a)
-      QSA_REG_CASE(topk_expand_reg_kernel, 96, kRT, grid, a)
-      default: QSA_REG_CASE(topk_expand_reg_kernel, 128, kRT, grid, a)
+      default: QSA_REG_CASE(topk_expand_reg_kernel, 72, kRT, grid, a)
     }
   }
   return hipGetLastError();

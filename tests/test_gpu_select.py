@@ -91,13 +91,16 @@ def test_topk_expand_prefill(qsa, O, case):
 # Long rows: name -> (B, S, numBlocks, ctx, rowStart, numRows, styles).  Their outputs span
 # B*S rows, so rows outside the chunk are checked on the device and only the chunk is copied.
 LONG_CASES = {
-    # 64 keys per thread: the long-prefill shape, rows at the end of a 131072-token sequence
+    # rows of 32758-32768 blocks at the end of a 131072-token sequence (one wave per row)
     "full32k": (1, 131072, 32768, [131072], 131072 - 40, 40,
                 ("scores", "normal", "ties", "special_ge", "zeros")),
     # 20 keys per thread (24 registers), mid-sequence rows
     "mid": (1, 40000, 10000, [40000], 20000, 64, ("scores", "normal", "ties", "special_ge")),
     # a chunk across two sequences: short rows of sequence 1 beside long rows of sequence 0
     "cross": (2, 12000, 3000, [12000, 11000], 11990, 30, ("scores", "normal")),
+    # rows of 18484-18500 blocks: just past the register kernel's 72 keys per thread
+    "past_registers": (1, 74000, 18500, [74000], 74000 - 64, 64,
+                       ("scores", "ties", "normal", "special_ge")),
     # rows longer than 32768 blocks (one wave per row, candidate buffer in LDS)
     "stream": (1, 140000, 35000, [140000], 140000 - 6, 6, ("scores", "normal", "ties")),
     # rows of about 70000 blocks: several cuts of the candidate buffer per row, with all keys
