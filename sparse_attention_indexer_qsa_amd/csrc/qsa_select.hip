@@ -662,8 +662,10 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
 // nothing, and several rows per CU overlap their loads with the others' selection.
 
 constexpr int kWaveRows = 4;       // rows (waves) per workgroup of the one-wave-per-row kernel
-constexpr int kWaveCap = 2048;     // candidate buffer entries per row (8 rows per CU)
-constexpr int kWaveKPL = 16;       // keys per lane per step (1024 keys)
+// (candidate buffer entries, keys per lane per step): rows of up to 32768 blocks keep 16 rows
+// per CU (36 KB of LDS per workgroup); longer ones a larger buffer and steps, so fewer cuts
+constexpr int kWaveCapMid = 1024, kWaveKPLMid = 4;    // 256 keys per step
+constexpr int kWaveCapLong = 1536, kWaveKPLLong = 8;  // 512 keys per step
 
 template <int kCap>
 struct WaveShared {
@@ -1218,12 +1220,22 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   // 32768 blocks: 176 against 224 us)
   if (kpt == 0 || kpt > kRegMaxKeys) {
     const dim3 wgrid((unsigned)((a.numRows + kWaveRows - 1) / kWaveRows));
-    if (aligned)
-      hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCap, kWaveKPL, true>), wgrid,
-                         dim3(64 * kWaveRows), 0, stream, a);
-    else
-      hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCap, kWaveKPL, false>), wgrid,
-                         dim3(64 * kWaveRows), 0, stream, a);
+    const dim3 wblock(64 * kWaveRows);
+    if (nMax <= 32768) {  // per 4096 rows of 20000 / 32768 blocks: 121 / 153 us (1536: 126 / 177)
+      if (aligned)
+        hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCapMid, kWaveKPLMid, true>), wgrid,
+                           wblock, 0, stream, a);
+      else
+        hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCapMid, kWaveKPLMid, false>), wgrid,
+                           wblock, 0, stream, a);
+    } else {  // per 2048 rows of 65536 blocks: 129 us (1024: 175)
+      if (aligned)
+        hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCapLong, kWaveKPLLong, true>), wgrid,
+                           wblock, 0, stream, a);
+      else
+        hipLaunchKernelGGL((topk_expand_wave_kernel<kWaveCapLong, kWaveKPLLong, false>), wgrid,
+                           wblock, 0, stream, a);
+    }
   } else {
     switch (kpt) {
       QSA_REG_CASE(topk_expand_reg_kernel, 4, kRT, grid, a)

@@ -98,6 +98,10 @@ LONG_CASES = {
     "mid": (1, 40000, 10000, [40000], 20000, 64, ("scores", "normal", "ties", "special_ge")),
     # a chunk across two sequences: short rows of sequence 1 beside long rows of sequence 0
     "cross": (2, 12000, 3000, [12000, 11000], 11990, 30, ("scores", "normal")),
+    # rows of 19999-20000 blocks beside every length from 0 to 1100 blocks of a second sequence
+    # (the 1024-entry candidate buffer of rows up to 32768 blocks) and its padded rows
+    "mid_buffer_edge": (2, 80000, 20000, [80000, 4400], 80000 - 4, 4 + 4500,
+                        ("scores", "ties", "normal", "special_ge")),
     # rows of 18484-18500 blocks: just past the register kernel's 72 keys per thread
     "past_registers": (1, 74000, 18500, [74000], 74000 - 64, 64,
                        ("scores", "ties", "normal", "special_ge")),
