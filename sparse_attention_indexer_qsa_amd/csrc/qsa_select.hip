@@ -910,6 +910,7 @@ __global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkAr
   constexpr int kStep = 64 * KPL;
   constexpr int kSlack = kCap - kStep - kTopK;  // a cut during the walk leaves room for a step
   static_assert(kCap % 256 == 0 && kSlack >= 0, "a step must fit a cut buffer");
+  static_assert(KPL % 4 == 0, "keys are loaded in 16-byte groups of 4 per lane");
   __shared__ WaveShared<kCap> shAll[kWaveRows];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
