@@ -21,7 +21,11 @@
  *  - Errors.  A non-zero return is one of the QSA_E_* codes; qsa_last_error() then returns a
  *    thread-local text describing it.  Validation failures are reported before any launch, so a
  *    call that returns QSA_E_INVALID / QSA_E_ALIGN / QSA_E_DTYPE has written nothing.
- *    QSA_E_LAUNCH means the HIP runtime refused the launch.
+ *    A call with valid arguments and work to do then checks for a current HIP device and
+ *    returns QSA_E_NO_DEVICE, having launched nothing, when there is none (no GPU visible or no
+ *    usable driver).  QSA_E_LAUNCH means the HIP runtime refused the launch (for instance a
+ *    device without gfx950 code objects).  These map the page's launchers, which throw on
+ *    invalid arguments or launch failure ("Qsa Indexer Kernels", each launcher's Throws).
  *  - Empty work.  batchSize == 0, an empty block range, or seqLen == 0 for q-prep returns
  *    QSA_OK without launching anything.
  *  - Device values outside the contract never fault: context lengths are clamped or treated as
@@ -48,7 +52,8 @@ enum {
   QSA_E_INVALID = -1, /* a null required pointer, a negative size, an inconsistent range    */
   QSA_E_ALIGN = -2,   /* a pointer or pool geometry that breaks the alignment rules above   */
   QSA_E_DTYPE = -3,   /* dt is not QSA_F16 or QSA_BF16                                        */
-  QSA_E_LAUNCH = -4   /* the HIP runtime rejected a kernel launch                             */
+  QSA_E_LAUNCH = -4,  /* the HIP runtime rejected a kernel launch                             */
+  QSA_E_NO_DEVICE = -5 /* no usable current HIP device (no GPU or no driver); nothing launched */
 };
 
 /* Fixed geometry of the method ("Qsa Indexer Kernels": launchQsaIndexQPrep and

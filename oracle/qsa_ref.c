@@ -17,10 +17,18 @@
  * step):
  *   - Build with -ffp-contract=off -fno-fast-math on x86-64 (SSE): every float operation below
  *     is one IEEE binary32 operation rounded to nearest even; no FMA, no reassociation.
- *   - The sum of squares (reduction order left open by the page) is accumulated in binary64,
- *     where each product of two widened T values is exact, and rounded once to binary32.
- *   - rsqrtf (an approximate intrinsic on the page's hardware) is taken as the correctly
- *     rounded binary32 value of 1/sqrt(v), evaluated in binary64 and rounded once.
+ *   - The sum of squares (reduction order left open by the page) is accumulated in binary64
+ *     and then rounded to binary32.  Each product of two widened T values is exact in
+ *     binary64; the running sum is exact too while the squares span less than 2^24 in
+ *     magnitude (2^30 for bf16, whose products have fewer bits), and otherwise within 127 * 2^-53 relative of the exact sum (positive terms),
+ *     so the binary32 result is the exact sum correctly rounded except within that distance of
+ *     a binary32 rounding midpoint.
+ *   - rsqrtf (an approximate intrinsic on the page's hardware) is taken as 1/sqrt(v) evaluated
+ *     in binary64 and then narrowed: three roundings (the binary64 square root, the binary64
+ *     division, the conversion to binary32).  The two binary64 steps leave a relative error
+ *     below 2^-52, so the result is the correctly rounded binary32 value except where the
+ *     exact 1/sqrt(v) lies within that distance of a binary32 rounding midpoint; either way it
+ *     is within 0.5 ulp + 2^-29 ulp of the exact value.
  *   - Conversions between binary32 and T are written below from the IEEE 754 definitions:
  *     widening is exact; narrowing rounds to nearest, ties to even, keeps subnormals, and maps
  *     NaN to a quiet NaN.
@@ -428,10 +436,11 @@ static float score_scale(void) {
 
 /*
  * Block relevance of one query token against one kbar row ("Qsa Indexer Kernels",
- * launchQsaIndexScores): per head h the FP32 dot q_h . kbar (products of T values are exact;
- * the sum, whose order the page leaves open, is taken exactly in binary64 and rounded once),
- * ReLU per head, the four heads summed in ascending h in binary32, then scaled by 1/sqrtf(128)
- * after the sum.
+ * launchQsaIndexScores): per head h the FP32 dot q_h . kbar (products of T values are exact
+ * in binary64; the sum, whose order the page leaves open, is accumulated in binary64, exact
+ * while the products span less than 2^24 (2^30 for bf16) in magnitude and otherwise within
+ * 127 * 2^-53 of the sum of their magnitudes, then rounded to binary32), ReLU per head, the
+ * four heads summed in ascending h in binary32, then scaled by 1/sqrtf(128) after the sum.
  */
 static float block_score(const uint16_t* q, const uint16_t* kb, int dt) {
   float sum = 0.0f;

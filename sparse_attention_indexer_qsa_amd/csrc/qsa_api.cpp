@@ -119,6 +119,17 @@ int check_range(int32_t numBlocks, int32_t blockBegin, int32_t blockEnd, int32_t
   return QSA_OK;
 }
 
+// A call that is about to launch needs a current HIP device: with no device (or no usable
+// driver) hipGetDevice reports an error, and the call returns QSA_E_NO_DEVICE having launched
+// nothing.  Runs after validation, so invalid arguments are reported as such on any machine.
+int device_ready() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(QSA_E_NO_DEVICE, "no usable HIP device: %s", hipGetErrorString(e));
+  return QSA_OK;
+}
+
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(QSA_E_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -148,6 +159,7 @@ int q_prep_impl(void* qNormed, const void* indexQk, const float* cosSin, int32_t
   }
   TRY(check_grid((int64_t)B * ceil_div(ceil_div(S, 4), 4)));
   const qsa::QPrepArgs a{qNormed, indexQk, cosSin, ctx, wQ, eps, B, S, meanSq, inv, preCast};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_q_prep(a, t, debug, static_cast<hipStream_t>(stream)),
                   "qsa_index_q_prep");
@@ -186,6 +198,7 @@ int k_compress_impl(void* kbar, const void* indexQk, const float* cosSin, int32_
   TRY(check_grid((int64_t)B * ceil_div(r.span, 16)));
   const qsa::KCompressArgs a{kbar, indexQk, cosSin, maxPositions, ctx, wK, eps, B, S, numBlocks,
                              r, p, mT, meanSq, inv, preCast};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_k_compress(a, t, debug, static_cast<hipStream_t>(stream)),
                   "qsa_index_k_compress");
@@ -255,6 +268,7 @@ QSA_EXPORT int qsa_index_persist(const qsa_pool_state_t* pool, const void* index
   const int64_t items = 3 + (kbar != nullptr ? (int64_t)r.span : 0);
   TRY(check_grid((int64_t)batchSize * ceil_div(items, 16)));
   const qsa::PersistArgs a{p, indexQk, kbar, contextLengths, batchSize, seqLen, numBlocks, r};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_persist(a, static_cast<hipStream_t>(stream)), "qsa_index_persist");
 }
@@ -288,6 +302,7 @@ QSA_EXPORT int qsa_index_prefill(void* qNormed, void* kbar, const void* indexQk,
   TRY(check_grid((int64_t)batchSize * ceil_div(ceil_div(seqLen, 4), 4)));
   const qsa::PrefillArgs a{qNormed, kbar, indexQk, cosSin, contextLengths, wQ, wK, rmsEps,
                            batchSize, seqLen, numBlocks, p};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_prefill(a, t, static_cast<hipStream_t>(stream)),
                   "qsa_index_prefill");
@@ -319,6 +334,7 @@ QSA_EXPORT int qsa_index_pre_decode(void* qNormed, const void* indexQk, const fl
   TRY(check_grid(batchSize));  // one workgroup per sequence
   const qsa::PreDecodeArgs a{qNormed, indexQk, cosSin, maxPositions, contextLengths, newLens,
                              wQ, wK, rmsEps, batchSize, seqLen, p};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_pre_decode(a, t, static_cast<hipStream_t>(stream)),
                   "qsa_index_pre_decode");
@@ -356,6 +372,7 @@ QSA_EXPORT int qsa_index_scores(float* logits, const void* qNormed, const void* 
   a.numRows = numRows;
   qsa::ScoresArgs probe = a;  // the launcher fills the tile fields the same way
   TRY(check_grid(qsa::scores_workgroups(probe), qsa::kScoresThreads));
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_scores(a, t, static_cast<hipStream_t>(stream)), "qsa_index_scores");
 }
@@ -378,6 +395,7 @@ QSA_EXPORT int qsa_index_scores_decode(float* logits, const void* qNormed,
   TRY(check_pool(pool, &p));
   TRY(check_grid(batchSize));  // grid (batchSize, ceil(maxBlocks / 64))
   const qsa::ScoresDecodeArgs a{logits, qNormed, contextLengths, p, batchSize, maxBlocks};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_scores_decode(a, t, static_cast<hipStream_t>(stream)),
                   "qsa_index_scores_decode");
@@ -404,6 +422,7 @@ QSA_EXPORT int qsa_index_ids_fill(int32_t* ids, int32_t numRows, int32_t numBloc
     return fail(QSA_E_INVALID, "numRows = %d, numBlocks = %d must be >= 0", numRows, numBlocks);
   if (numRows == 0 || numBlocks == 0) return ok();
   TRY(need(ids, "ids", 4));
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_ids_fill(ids, (int64_t)numRows * numBlocks, numBlocks,
                                        static_cast<hipStream_t>(stream)),
@@ -425,6 +444,7 @@ QSA_EXPORT int qsa_index_expand(int32_t* outIdx, const int32_t* sortedIds,
   TRY(need(contextLengths, "contextLengths", 4));
   TRY(check_grid(numRows));
   const qsa::ExpandArgs a{outIdx, sortedIds, contextLengths, seqLen, numBlocks, rowStart, numRows};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_expand(a, static_cast<hipStream_t>(stream)), "qsa_index_expand");
 }
@@ -440,6 +460,7 @@ QSA_EXPORT int qsa_index_topk_expand(int32_t* outIdx, const float* logits,
   TRY(need(contextLengths, "contextLengths", 4));
   TRY(check_grid(numRows));
   const qsa::TopkArgs a{outIdx, logits, contextLengths, seqLen, numBlocks, rowStart, numRows};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_topk_expand(a, static_cast<hipStream_t>(stream)),
                   "qsa_index_topk_expand");
@@ -462,6 +483,7 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
   TRY(check_grid(batchSize, 512));  // one 512-thread workgroup per sequence
   const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
                               splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_topk_expand_decode(a, static_cast<hipStream_t>(stream)),
                   "qsa_index_topk_expand_decode");
@@ -475,6 +497,7 @@ QSA_EXPORT int qsa_stream_copy(void* dst, const void* src, int64_t bytes, void* 
   TRY(need(dst, "dst", 16));
   TRY(need(src, "src", 16));
   TRY(check_grid((bytes / 16 + 255) / 256));
+  TRY(device_ready());
   (void)hipGetLastError();
   return launched(qsa::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream)),
                   "qsa_stream_copy");

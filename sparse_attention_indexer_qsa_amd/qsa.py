@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
 QSA_F16, QSA_BF16 = 0, 1
-QSA_OK, QSA_E_INVALID, QSA_E_ALIGN, QSA_E_DTYPE, QSA_E_LAUNCH = 0, -1, -2, -3, -4
+QSA_OK, QSA_E_INVALID, QSA_E_ALIGN, QSA_E_DTYPE, QSA_E_LAUNCH, QSA_E_NO_DEVICE = \
+    0, -1, -2, -3, -4, -5
 ROW_WIDTH, HEAD_DIM, HEADS = 640, 128, 4
 TOPK, INDEX_WIDTH = 512, 2051
 

@@ -68,31 +68,50 @@ def widen(bits, dt):
     return bits.view(np.float16).astype(np.float64)
 
 
-def compare_T(got, ref, dt, pre=None, cs=None, what=""):
-    """Normed/roped outputs: at most 1 ulp of T apart.  Where rope cancels
-    (|o| < 2^-6 (|y_a c| + |y_b s|)), the allowance is 1 ulp(o) + 2^-22 (|y_a c| + |y_b s|),
-    with |y_a c| + |y_b s| bounded by (|c| + |s|) * |(o_a, o_b)| from the oracle's pre-cast
-    pair.  `pre` [..., 128] FP32 and `cs` [..., 64] (the cosSin row of each vector) enable the
-    cancellation clause.  Returns the number of elements that differ in any bit."""
+def rope_terms(pre, cs):
+    """|y_a c| + |y_b s| for every element of roped vectors, the magnitude of the two products
+    whose difference (or sum) is the element: o_a = y_a c - y_b s and o_b = y_b c + y_a s for
+    the pair (a, b) = (i, i+32), i < 32.  The pre-rope pair (y_a, y_b) is recovered in float64
+    from the oracle's pre-cast pair by the inverse rotation (y_a = o_a c + o_b s,
+    y_b = o_b c - o_a s; the cosSin rows satisfy c^2 + s^2 = 1 to binary32 rounding).  Dims
+    [64, 128) are not roped: their term is |o| itself.  `pre` [N, 128], `cs` [N, 64]."""
+    pre = np.asarray(pre, np.float64).reshape(-1, 128)
+    cs = np.asarray(cs, np.float64).reshape(-1, 64)
+    c, s = cs[:, :32], cs[:, 32:]
+    oa, ob = pre[:, :32], pre[:, 32:64]
+    ya, yb = oa * c + ob * s, ob * c - oa * s
+    M = np.abs(pre).copy()
+    M[:, :32] = np.abs(ya * c) + np.abs(yb * s)
+    M[:, 32:64] = np.abs(yb * c) + np.abs(ya * s)
+    return M
+
+
+def compare_T(got, ref, dt, pre=None, cs=None, what="", stats=None):
+    """Normed/roped outputs: at most 1 ulp of T apart.  On rope dims where the two products
+    cancel, |o| < 2^-6 (|y_a c| + |y_b s|), the allowance is 1 ulp(o) + 2^-22 (|y_a c| + |y_b s|)
+    (rope_terms).  `pre` [..., 128] FP32 (the oracle's pre-cast values) and `cs` [..., 64] (the
+    cosSin row of each vector) enable that clause.  Returns the number of elements that differ
+    in any bit; with `stats` (a dict) also records how many elements are within 1 ulp only
+    ("ulp1") and how many pass only by the cancellation clause ("cancel")."""
     got, ref = np.asarray(got).reshape(-1, 128), np.asarray(ref).reshape(-1, 128)
     both_nan = is_nan(got, dt) & is_nan(ref, dt)
     d = np.abs(ordered(got) - ordered(ref))
     bad = (d > 1) & ~both_nan
+    n_cancel = 0
     if bad.any() and pre is not None:
-        pre = np.asarray(pre, np.float64).reshape(-1, 128)
-        cs = np.asarray(cs, np.float64).reshape(-1, 64)
-        c, s = np.abs(cs[:, :32]), np.abs(cs[:, 32:])
-        pair = np.sqrt(pre[:, :32] ** 2 + pre[:, 32:64] ** 2)
-        M = np.zeros_like(pre)
-        M[:, :32] = (c + s) * pair
-        M[:, 32:64] = (c + s) * pair
-        o = pre
+        o = np.asarray(pre, np.float64).reshape(-1, 128)
+        M = rope_terms(o, cs)
+        M[:, 64:] = 0.0                      # the clause covers roped dims only
         cancel = np.abs(o) < 2.0 ** -6 * M
         allow = ulp_value(ref, dt) + 2.0 ** -22 * M
-        ok = cancel & (np.abs(widen(got, dt) - o) <= allow)
+        ok = bad & cancel & (np.abs(widen(got, dt) - o) <= allow)
+        n_cancel = int(ok.sum())
         bad &= ~ok
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond tolerance, e.g. at " \
         f"{np.argwhere(bad)[:5].tolist()} got {got[bad][:5]} ref {ref[bad][:5]}"
+    if stats is not None:
+        stats["ulp1"] = int(((d == 1) & ~both_nan).sum())
+        stats["cancel"] = n_cancel
     return int((got != ref).sum())
 
 

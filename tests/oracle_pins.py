@@ -644,6 +644,18 @@ def _orderable_np(lg):
     return np.where(b & 0x80000000, (~b) & 0xFFFFFFFF, b | 0x80000000)
 
 
+def check_ids_fill(O):
+    """launchQsaIndexIdsFill: every row of the segmented sort's id array is 0, 1, ...,
+    numBlocks-1 (the page's ids[r * numBlocks + c] = c), whatever the row; empty shapes give
+    empty arrays.  The 3 x 5 case is written out by hand."""
+    assert O.ids_fill(3, 5).tolist() == [[0, 1, 2, 3, 4]] * 3
+    assert O.ids_fill(1, 1).tolist() == [[0]]
+    assert O.ids_fill(0, 7).shape == (0, 7) and O.ids_fill(4, 0).shape == (4, 0)
+    big = O.ids_fill(37, 1031)
+    assert np.all(big[:, 0] == 0) and np.all(np.diff(big, axis=1) == 1)
+    assert np.all(big == big[:1])
+
+
 def check_expand_hand_worked(O):
     """launchQsaIndexExpand on hand-worked rows: t=0 is only its tail token; t=3 one block; t=6
     one block plus tail 4,5,6; t=2050 fills all 2051 slots (4*512 + 3); a padded row is -1."""

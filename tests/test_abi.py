@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(qsa):
 def test_abi_version_and_codes(qsa):
     assert qsa.qsa_abi_version() == _header_int("QSA_ABI_VERSION")
     for n in ("QSA_OK", "QSA_E_INVALID", "QSA_E_ALIGN", "QSA_E_DTYPE", "QSA_E_LAUNCH",
-              "QSA_F16", "QSA_BF16"):
+              "QSA_E_NO_DEVICE", "QSA_F16", "QSA_BF16"):
         assert getattr(qsa, n) == _header_int(n), n
 
 
@@ -131,8 +131,8 @@ def _kcomp(qsa, h, pool=None, ranges=None, **kw):
 def test_k_compress_validation(qsa, host, kw, code):
     rc = _kcomp(qsa, host, **kw)
     if code == "QSA_OK_IF_NO_GPU":
-        # maxPositions = 4*blockEnd - 3 passes validation; with no GPU the launch itself fails
-        assert rc == qsa.QSA_E_LAUNCH
+        # maxPositions = 4*blockEnd - 3 passes validation; with no GPU nothing is launched
+        assert rc == qsa.QSA_E_NO_DEVICE
     else:
         assert rc == getattr(qsa, code)
 
@@ -189,7 +189,7 @@ def test_persist_and_prefill_validation(qsa, host):
                                    a["dt"], None)
     assert pre(nb=15) == qsa.QSA_E_INVALID
     assert pre(S=61, nb=15) == qsa.QSA_E_INVALID         # ceilDiv(61, 4) = 16 > 15
-    assert pre(S=60, nb=15) == qsa.QSA_E_LAUNCH          # valid; with no GPU the launch fails
+    assert pre(S=60, nb=15) == qsa.QSA_E_NO_DEVICE       # valid; no GPU here: no launch
     assert pre(P=63) == qsa.QSA_E_INVALID
     assert pre(wk=None) == qsa.QSA_E_INVALID
     assert pre(dt=2) == qsa.QSA_E_DTYPE
@@ -280,3 +280,37 @@ def test_stream_copy_validation(qsa, host):
     assert L.qsa_stream_copy(h.p(0, 8), h.p(1), 32, None) == qsa.QSA_E_ALIGN
     assert L.qsa_stream_copy(h.p(0), h.p(1, 4), 32, None) == qsa.QSA_E_ALIGN
     assert L.qsa_stream_copy(None, None, 0, None) == qsa.QSA_OK
+
+
+def test_valid_calls_report_no_device(qsa, host):
+    """Every entry point, given valid arguments and work to do on a machine with no GPU,
+    returns QSA_E_NO_DEVICE (nothing launched) with a message naming the cause."""
+    L, h, BF = qsa.lib, host, qsa.QSA_BF16
+    pool = ctypes.byref(_pool(qsa, h))
+    ND = qsa.QSA_E_NO_DEVICE
+    calls = {
+        "q_prep": lambda: _qprep(qsa, h),
+        "k_compress": lambda: _kcomp(qsa, h),
+        "k_compress_paged": lambda: _kcomp(qsa, h, pool=_pool(qsa, h)),
+        "persist": lambda: L.qsa_index_persist(pool, h.p(1), None, h.p(3), 2, 64, 16, 0, 16, 0,
+                                               None, BF, None),
+        "prefill": lambda: L.qsa_index_prefill(h.p(0), h.p(1), h.p(2), h.p(3), 64, h.p(4),
+                                               h.p(5), h.p(6), 1e-6, None, 2, 64, 16, BF, None),
+        "pre_decode": lambda: L.qsa_index_pre_decode(h.p(0), h.p(1), h.p(2), 64, h.p(3), None,
+                                                     h.p(4), h.p(8), 1e-6, pool, 2, 4, BF,
+                                                     None),
+        "scores": lambda: L.qsa_index_scores(h.p(0), h.p(1), h.p(2), h.p(3), 2, 64, 16, 0, 128,
+                                             BF, None),
+        "scores_decode": lambda: L.qsa_index_scores_decode(h.p(0), h.p(1), h.p(3), pool, 2, 16,
+                                                           BF, None),
+        "ids_fill": lambda: L.qsa_index_ids_fill(h.p(0), 4, 16, None),
+        "expand": lambda: L.qsa_index_expand(h.p(0), h.p(1), h.p(3), 2, 64, 16, 0, 128, None),
+        "topk_expand": lambda: L.qsa_index_topk_expand(h.p(0), h.p(1), h.p(3), 2, 64, 16, 0,
+                                                       128, None),
+        "topk_expand_decode": lambda: L.qsa_index_topk_expand_decode(h.p(0), h.p(1), h.p(3),
+                                                                     None, 0, 2, 1000, None),
+        "stream_copy": lambda: L.qsa_stream_copy(h.p(0), h.p(1), 64, None),
+    }
+    for name, call in calls.items():
+        assert call() == ND, name
+        assert "no usable HIP device" in qsa.qsa_last_error(), name

@@ -116,6 +116,11 @@ LONG_CASES = {
     # 2048), and its padded rows
     "long_unaligned": (2, 131080, 32771, [131080, 8196], 131080 - 4, 4 + 8250,
                        ("scores", "ties", "normal", "special_ge")),
+    # the 1024-entry candidate buffer on numBlocks not a multiple of 4 (one load per key):
+    # eight rows of 19999-20001 blocks beside every length from 0 to 775 blocks of a second
+    # sequence, and its padded rows
+    "wave_unaligned": (2, 80004, 20001, [80004, 3100], 80004 - 8, 8 + 3200,
+                       ("scores", "ties", "normal", "special_ge")),
     # numBlocks not a multiple of 4 (one load per key): eight rows of 2249-2251 blocks beside
     # every length from 0 to 1750 blocks of a second sequence, and its padded rows
     "unaligned": (2, 9004, 2251, [9004, 7000], 9004 - 8, 8 + 7100,

@@ -66,6 +66,10 @@ MUTANTS = {
                                   "      for (int64_t i = 0; i < kSel; ++i) sel[n++] = kv[i].id;"),
     "expand_padded_rule": ("    if (ctx[b] <= 0 || t >= ctx[b]) {\n      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;\n      continue;\n    }\n    int64_t nVis = (t + 1) / 4;\n    expand_row(out, sortedIds",
                            "    if (ctx[b] <= 0 || t > ctx[b]) {\n      for (int k = 0; k < INDEX_WIDTH; ++k) out[k] = -1;\n      continue;\n    }\n    int64_t nVis = (t + 1) / 4;\n    expand_row(out, sortedIds"),
+    "ids_fill_flat_iota": ("for (int64_t c = 0; c < numBlocks; ++c) ids[r * numBlocks + c] = (int32_t)c;",
+                           "for (int64_t c = 0; c < numBlocks; ++c) ids[r * numBlocks + c] = (int32_t)(r * numBlocks + c);"),
+    "ids_fill_from_one": ("for (int64_t c = 0; c < numBlocks; ++c) ids[r * numBlocks + c] = (int32_t)c;",
+                          "for (int64_t c = 0; c < numBlocks; ++c) ids[r * numBlocks + c] = (int32_t)(c + 1);"),
     "rsqrt_single": ("float inv = (float)(1.0 / sqrt((double)v));",
                      "float inv = 1.0f / (float)sqrt((double)v) * (1.0f + 1.2e-7f);"),
 }
