@@ -12,7 +12,10 @@ every buffer, so no step finds its inputs in the 256 MB Infinity Cache.
 Prints one JSON line: rows/s (value), ms per step, the roofline of the kernel (algorithmic
 bytes per launch / average launch time from HIP events recorded on the launch stream, against
 the 8 TB/s HBM peak), HBM traffic measured by rocprofv3 counters when a committed profile of
-the current kernel source exists, and the CPU oracle timed on the host's cores.
+the current kernel source exists, and the CPU oracle timed on the host's cores.  Beside the
+headline: the block-scores and selection legs, the decode legs, and each of the other four
+workloads (tiny prefill, batched prefill in bf16 and fp16, decode sub-range compression,
+mixed serving step) timed with a cold cache per rep.
 """
 import argparse
 import ctypes
@@ -60,12 +63,71 @@ def algorithmic_bytes(wl):
     return k1a + k1b + persist + 2 * 256 + 4 * B
 
 
-def three_call_bytes(wl):
-    """The same count with the cosSin rows of block positions counted again for K1b (once
-    per call that consumes them, as for the three-call sequence)."""
+def _triplets(wl):
+    """Each sequence's block range [gB, gE) and past length: the call's scalars, or the
+    per-sequence arrays (the range capped at maxBlockSpan blocks)."""
     import numpy as np
-    L = np.clip(wl.ctx.astype(np.int64), 0, wl.S)
-    return algorithmic_bytes(wl) + 256 * int((L // 4).max())
+    B = wl.B
+    if wl.ranges is None:
+        return (np.full(B, wl.blockBegin, np.int64), np.full(B, wl.blockEnd, np.int64),
+                np.full(B, wl.pastLen, np.int64))
+    pl, bb, be, span = wl.ranges
+    bb = bb.astype(np.int64)
+    return bb, np.minimum(be.astype(np.int64), bb + span), pl.astype(np.int64)
+
+
+def path_bytes(wl, q_prep=True):
+    """Algorithmic bytes of one pass of the path over workload `wl`, from its seeded lengths
+    and page table (an unfused sequence of calls is scored against the same count):
+      q-prep   1024 per valid q row read + 256 per distinct cosSin row + 1024 per qNormed row
+               written (padding zeros included);
+      compress 1024 per valid block's raw keys + 256 per distinct cosSin row 4g + 256 per dense
+               kbar row of the range written (invalid zeros included);
+      persist  512 per raw-K tail token copied + 256 per kbar V-tail written + 4 per distinct
+               page-table entry read;
+      plus the two gammas (512) and the lengths (4 per sequence).
+    Writes whose page entry is unused or out of range are not counted (nothing moves)."""
+    import numpy as np
+    B, S, nb = wl.B, wl.S, wl.numBlocks
+    ctx = wl.ctx.astype(np.int64)
+    pt = wl.pool.pageTable.astype(np.int64)
+    mp, ids = pt.shape[2], 2 * wl.pool.numPages
+    k1a = 0
+    if q_prep:
+        L = np.clip(ctx, 0, S)
+        k1a = 1024 * int(L.sum()) + 256 * int(L.max(initial=0)) + 1024 * B * S
+    gB, gE, p = _triplets(wl)
+    valid_rows, dense, n_tail, n_kbar, entries = set(), 0, 0, 0, set()
+    n_valid = 0
+
+    def guard(b, plane, pos):
+        slot = pos >> 7
+        if slot < 0 or slot >= mp:
+            return False
+        entries.add((b, plane, slot))
+        e = int(pt[b, plane, slot])
+        return 0 <= e < ids
+
+    for b in range(B):
+        g = np.arange(max(gB[b], 0), min(gE[b], nb), dtype=np.int64)
+        dense += len(g)
+        t0 = 4 * g
+        ok = (t0 + 3 < ctx[b]) & (t0 >= p[b]) & (t0 + 3 - p[b] < S)
+        if wl.ranges is not None:
+            ok &= t0 < wl.maxPositions
+        gv = g[ok]
+        n_valid += len(gv)
+        valid_rows.update((4 * gv).tolist())
+        for pos in (4 * gv).tolist():
+            n_kbar += guard(b, 1, pos)
+        c = int(ctx[b])
+        if c > 0:
+            for t in range(max(int(p[b]), c - c % 4), c):
+                if 0 <= t - p[b] < S:
+                    n_tail += guard(b, 0, t)
+    k1b = 1024 * n_valid + 256 * len(valid_rows) + 256 * dense
+    persist = 512 * int(n_tail) + 256 * int(n_kbar) + 4 * len(entries)
+    return int(k1a + k1b + persist + 2 * 256 + 4 * B)
 
 
 SCORE_ROWS = (65536, 8192)   # the long prefill's query rows [65536, 73728) scored and selected
@@ -177,6 +239,103 @@ def decode_leg(qsa, torch, steps, warmup):
     return {"workload": "decode pre-pass, B=64, one new token each, bf16",
             "entry": "qsa_index_pre_decode", "us_per_call": us, "tokens_per_s": B / us * 1e6,
             "blocks_compressed_per_call": blocks}
+
+
+CONFIG_LEGS = ("tiny_prefill", "batched_prefill_bf16", "batched_prefill_f16", "decode_subrange",
+               "mixed_serving")
+SCRATCH_BYTES = 512 << 20    # written between cold-cache reps: twice the 256 MB Infinity Cache
+
+
+def _config_workload(name):
+    from sparse_attention_indexer_qsa_amd import workloads as W
+    return {"tiny_prefill": W.config1, "batched_prefill_bf16": lambda: W.config2("bf16"),
+            "batched_prefill_f16": lambda: W.config2("f16"), "decode_subrange": W.config4,
+            "mixed_serving": W.config5}[name]()
+
+
+def config_leg(qsa, torch, name, reps, warmup):
+    """One of the five workloads through the C ABI, each rep with a cold cache: a 512 MiB
+    scratch write (outside the timed span) evicts the Infinity Cache, then HIP events on the
+    launch stream bracket the rep.  Prefills run as one fused launch (qsa_index_prefill) and
+    as the three calls (q-prep, block compression with the pool, persist); the decode
+    sub-range runs block compression with per-sequence ranges and the pool, then persist.
+    Median, p10 and p90 over `reps`; GB/s on path_bytes of the run's seeded lengths."""
+    import numpy as np
+    wl = _config_workload(name)
+    T = qsa.QSA_BF16 if wl.dt == "bf16" else qsa.QSA_F16
+    B, S, nb = wl.B, wl.S, wl.numBlocks
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    x, cs = bits(wl.indexQk), torch.from_numpy(wl.cosSin).cuda()
+    ctx, wQ, wK = torch.from_numpy(wl.ctx).cuda(), bits(wl.wQ), bits(wl.wK)
+    pool = torch.full(wl.pool.shape, 0xA5A5 - 65536, dtype=torch.int16, device="cuda")
+    ps = qsa.PoolState(pool, torch.from_numpy(wl.pool.pageTable).cuda(), wl.pool.numPages,
+                       wl.pool.numKVHeads, wl.pool.poolHeadDim, wl.pool.headSize)
+    pst = ps.c_struct(B)
+    q = torch.empty(B, S, 4, 128, dtype=torch.int16, device="cuda")
+    kb = torch.empty(B, nb, 128, dtype=torch.int16, device="cuda")
+    rng = None
+    if wl.ranges is not None:
+        pl, bb, be, span = wl.ranges
+        rt = [torch.from_numpy(a).cuda() for a in (pl, bb, be)]
+        rng = qsa.qsa_seq_ranges_t(rt[0].data_ptr(), rt[1].data_ptr(), rt[2].data_ptr(), span)
+    rp = ctypes.byref(rng) if rng is not None else None
+    scratch = torch.empty(SCRATCH_BYTES // 4, dtype=torch.float32, device="cuda")
+    L = qsa.lib
+    alg = path_bytes(wl, wl.run_q_prep)
+
+    def fused(st):
+        return L.qsa_index_prefill(q.data_ptr(), kb.data_ptr(), x.data_ptr(), cs.data_ptr(),
+                                   cs.shape[0], ctx.data_ptr(), wQ.data_ptr(), wK.data_ptr(),
+                                   wl.eps, ctypes.byref(pst), B, S, nb, T, st)
+
+    def three(st):
+        rc = 0
+        if wl.run_q_prep:
+            rc |= L.qsa_index_q_prep(q.data_ptr(), x.data_ptr(), cs.data_ptr(), cs.shape[0],
+                                     ctx.data_ptr(), wQ.data_ptr(), wl.eps, B, S, T, st)
+        rc |= L.qsa_index_k_compress(kb.data_ptr(), x.data_ptr(), cs.data_ptr(), cs.shape[0],
+                                     ctx.data_ptr(), wK.data_ptr(), wl.eps, B, S, nb,
+                                     wl.blockBegin, wl.blockEnd, wl.pastLen, rp,
+                                     ctypes.byref(pst), T, st)
+        rc |= L.qsa_index_persist(ctypes.byref(pst), x.data_ptr(), None, ctx.data_ptr(), B, S, nb,
+                                  wl.blockBegin, wl.blockEnd, wl.pastLen, rp, T, st)
+        return rc
+
+    def cold(fn):
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                assert fn(stream.cuda_stream) == 0, qsa.qsa_last_error()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for i, (a, b) in enumerate(ev):
+                scratch.fill_(float(i))
+                a.record(stream)
+                fn(stream.cuda_stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        p10, p50, p90 = us[len(us) // 10], us[len(us) // 2], us[(9 * len(us)) // 10]
+        return {"us_p10_p50_p90": [p10, p50, p90], "rows_per_s": B * S / p50 * 1e6,
+                "GBps": alg / p50 / 1e3, "hbm_frac": alg / p50 / 1e3 / HBM_PEAK_GBPS}
+
+    out = {"workload": f"{wl.name}: B={B}, S={S}, {wl.dt}, numBlocks={nb}, "
+                       f"numPages={wl.pool.numPages}", "alg_bytes": alg,
+           "valid_rows": int(np.clip(wl.ctx, 0, S).sum()) if wl.run_q_prep else None}
+    if wl.ranges is None:
+        out["fused"] = cold(fused)
+        out["fused"]["entry"] = "qsa_index_prefill"
+    out["three_call"] = cold(three)
+    out["three_call"]["entry"] = ("qsa_index_q_prep + " if wl.run_q_prep else "") + \
+        "qsa_index_k_compress (pool" + (", per-sequence ranges" if rng is not None else "") + \
+        ") + qsa_index_persist"
+    del pool, scratch, x, q, kb
+    torch.cuda.empty_cache()
+    return out
 
 
 def _time_stream(torch, fn, steps, warmup):
@@ -519,6 +678,96 @@ def summarize_next(stats, fetch, write, f_scale, w_scale):
     print("\n".join(md))
 
 
+CONFIG_MD = os.path.join(ROOT, "profiles", "config_legs.md")
+CONFIG_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/ctrace_$LEG -o run -- "
+             "python3 $R/bench.py --only $LEG --steps 50 --warmup 5",
+    "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/cfetch_$LEG -o run "
+             "-- python3 $R/bench.py --only $LEG --steps 10 --warmup 2 --copy-calib",
+    "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/cwrite_$LEG -o run "
+             "-- python3 $R/bench.py --only $LEG --steps 10 --warmup 2 --copy-calib",
+}
+
+
+def summarize_configs(out_dir):
+    """profiles/ summary of the five-workload legs: for each, the library's kernels from its
+    own kernel trace and FETCH_SIZE / WRITE_SIZE runs (CONFIG_CMDS), counters scaled by what
+    they read for the 256 MiB torch.mul reference of the same run; per step, the kernels of the
+    fused launch and of the call sequence against the path's algorithmic bytes."""
+    md = ["# The five workloads: kernel durations and HBM traffic", "",
+          "MI355X (gfx950), one GPU.  One profiler run per workload and per counter; commands "
+          "(from `/tmp`, `TMPDIR=/tmp`; `R` the repository root, `OUT` the profiler output "
+          "directory, `LEG` the workload name):", ""]
+    md += ["    " + c for c in CONFIG_CMDS.values()]
+    md += ["", "Algorithmic bytes: the path's count for the run's seeded lengths and page table "
+           "(`bench.path_bytes`): q rows read, distinct cosSin rows, every qNormed row written, "
+           "raw keys of valid blocks, distinct cosSin rows of block positions, every kbar row "
+           "of the range, raw-K tails (read + write), V-tails written, page entries read, "
+           "gammas and lengths.  A kernel's 'measured' bytes are FETCH_SIZE and WRITE_SIZE per "
+           "dispatch, scaled.", ""]
+    ours = ("prefill_kernel", "q_prep_kernel", "k_compress_kernel", "persist_kernel")
+    for leg in CONFIG_LEGS:
+        tdir = os.path.join(out_dir, f"ctrace_{leg}")
+        if not os.path.isdir(tdir):
+            continue
+        wl = _config_workload(leg)
+        alg = path_bytes(wl, wl.run_q_prep)
+        stats = _csv_rows(tdir, "kernel_stats.csv")
+        fetch = _counter(os.path.join(out_dir, f"cfetch_{leg}"), "FETCH_SIZE")
+        write = _counter(os.path.join(out_dir, f"cwrite_{leg}"), "WRITE_SIZE")
+
+        def pick(d, key):
+            ks = [k for k in d if key in k]
+            return d[ks[0]][0] if ks else None
+        f_scale = COPY_BYTES / (pick(fetch, "MulFunctor") * 1024)
+        w_scale = COPY_BYTES / (pick(write, "MulFunctor") * 1024)
+        md += [f"## {leg}: B={wl.B}, S={wl.S}, {wl.dt}", "",
+               f"Algorithmic bytes per step: {alg:,}.  Counter scales: FETCH_SIZE x "
+               f"{f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.", "",
+               "| kernel | calls | avg us | measured bytes (fetch + write) |", "|---|---|---|---|"]
+        fused_us = seq_us = 0.0
+        fused_b = seq_b = 0.0
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            key = next((k for k in ours if k in r["Name"]), None)
+            if key is None:
+                continue
+            name = r["Name"].replace("qsa::(anonymous namespace)::", "").split("(")[0]
+            us = float(r["AverageNs"]) / 1e3
+            fk = [v for k, v in fetch.items() if k == r["Name"]]
+            wk = [v for k, v in write.items() if k == r["Name"]]
+            mb = None
+            if fk and wk:
+                mb = fk[0][0] * 1024 * f_scale + wk[0][0] * 1024 * w_scale
+            md.append(f"| `{name[:70]}` | {r['Calls']} | {us:.2f} | "
+                      + (f"{mb:,.0f} ({fk[0][0] * 1024 * f_scale:,.0f} + "
+                         f"{wk[0][0] * 1024 * w_scale:,.0f})" if mb is not None else "—") + " |")
+            if key == "prefill_kernel":
+                fused_us += us
+                fused_b += mb or 0.0
+            else:
+                seq_us += us
+                seq_b += mb or 0.0
+        md.append("")
+        for label, us, b in (("fused launch", fused_us, fused_b), ("call sequence", seq_us,
+                                                                    seq_b)):
+            if us > 0:
+                md.append(f"- {label}: {us:.2f} us of kernel time per step = "
+                          f"{alg / us / 1e3:,.0f} GB/s = {100 * alg / us / 1e3 / HBM_PEAK_GBPS:.1f} % "
+                          f"of 8 TB/s on the algorithmic bytes; measured {b:,.0f} B "
+                          f"({100 * (b - alg) / alg:+.1f} % vs algorithmic).")
+        md.append("")
+    md += ["Written by `python bench.py --summarize-configs $OUT`."]
+    open(CONFIG_MD, "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+def _json_default(o):
+    """numpy scalars in the result record become plain numbers."""
+    if hasattr(o, "item"):
+        return o.item()
+    raise TypeError(f"{type(o)} is not JSON serializable")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -533,12 +782,23 @@ def main():
     ap.add_argument("--no-scores", action="store_true", help="skip the block-scores leg")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the cold-cache legs of the five workloads")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated workload legs to run alone (of: "
+                         + ", ".join(CONFIG_LEGS) + "); prints their results only")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary and traffic record from rocprofv3 output "
                          "(kernel trace, FETCH_SIZE run, WRITE_SIZE run) and exit")
+    ap.add_argument("--summarize-configs", metavar="OUT",
+                    help="write profiles/config_legs.md from the per-workload rocprofv3 runs "
+                         "under OUT (ctrace_LEG, cfetch_LEG, cwrite_LEG) and exit")
     args = ap.parse_args()
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.summarize_configs:
+        summarize_configs(args.summarize_configs)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -556,6 +816,31 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    def copy_calib():
+        # a plain streaming kernel of known traffic: reads COPY_BYTES, writes COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+
+    def config_legs(names):
+        res = {}
+        for name in names:
+            print(f"[bench] timing the {name} workload (cold cache)", file=sys.stderr,
+                  flush=True)
+            res[name] = config_leg(qsa, torch, name, min(args.steps, 50), min(args.warmup, 5))
+        return res
+
+    if args.only:
+        names = [n for n in args.only.split(",") if n]
+        assert all(n in CONFIG_LEGS for n in names), (names, CONFIG_LEGS)
+        if args.copy_calib:
+            copy_calib()
+        print(json.dumps({"configs": config_legs(names)}, default=_json_default), flush=True)
+        return
+
     print("[bench] generating the long-prefill workload", file=sys.stderr, flush=True)
     wl = W.config3()
     B, S, nb = wl.B, wl.S, wl.numBlocks
@@ -637,14 +922,9 @@ def main():
         print("[bench] timing the three-call sequence", file=sys.stderr, flush=True)
         w3, e3 = timed(lambda i: three_calls(sets[i]), args.steps, args.warmup)
         three = {"ms_per_step": w3 * 1e3, "event_ms_per_step": e3 * 1e3,
-                 "rows_per_s": B * S / w3, "GBps_alg": three_call_bytes(wl) / e3 / 1e9}
+                 "rows_per_s": B * S / w3, "GBps_alg": path_bytes(wl) / e3 / 1e9}
     if args.copy_calib:
-        # a plain streaming kernel of known traffic: reads COPY_BYTES, writes COPY_BYTES
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
+        copy_calib()
 
     scores = select = select_long = select_decode = scores_decode = None
     if not args.no_scores:
@@ -666,10 +946,15 @@ def main():
         torch.cuda.empty_cache()
         decode = decode_leg(qsa, torch, args.steps, args.warmup)
 
-    alg = algorithmic_bytes(wl)
+    configs = None
+    if not args.no_configs:
+        configs = config_legs(CONFIG_LEGS)
+
+    alg = path_bytes(wl)                 # the path's algorithmic bytes of one step
+    alg_fused = algorithmic_bytes(wl)    # what the fused launch itself must move
     achieved = alg / ev / 1e9
     print("[bench] timing the copy reference", file=sys.stderr, flush=True)
-    copy_ref = copy_reference(qsa, torch, alg, min(args.steps, 100), min(args.warmup, 10))
+    copy_ref = copy_reference(qsa, torch, alg_fused, min(args.steps, 100), min(args.warmup, 10))
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
@@ -682,14 +967,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": "long_prefill", "B": B, "S": S, "T": "bf16", "theta": 1e6,
                    "numBlocks": nb, "numPages": wl.pool.numPages, "entry": "qsa_index_prefill",
-                   "buffer_sets": args.sets},
+                   "buffer_sets": args.sets,
+                   "timers": "value and ms_per_step: host wall clock around the timed launches "
+                             "(synchronised before and after); roofline.achieved: HIP events "
+                             "on the launch stream over the same launches"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "alg_bytes": alg, "event_us": ev * 1e6,
+                     "fused_launch_bytes": alg_fused,
+                     "frac_on_fused_launch_bytes": alg_fused / ev / 1e9 / HBM_PEAK_GBPS},
         "kernel": {"name": "prefill_kernel<Bf16, pool>", "alg_bytes_per_launch": alg,
+                   "fused_launch_bytes": alg_fused,
                    "event_us_per_launch": ev * 1e6,
                    "us_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2],
                                       per[(9 * len(per)) // 10]],
-                   "GBps_vs_three_call_bytes": three_call_bytes(wl) / ev / 1e9,
                    "source_sha256_16": kernel_source_hash(), "copy_reference": copy_ref},
         "three_call": three,
         "decode_pre_pass": decode,
@@ -698,13 +989,14 @@ def main():
         "select_long_rows": select_long,
         "scores_decode": scores_decode,
         "select_decode": select_decode,
+        "configs": configs,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out, default=_json_default), flush=True)
 
 
 if __name__ == "__main__":
