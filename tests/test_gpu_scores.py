@@ -177,6 +177,25 @@ def test_scores_narrow_numblocks(qsa, O):
     check_logits(got, ref, _abs_bound(q, kb, dt, np.arange(B * S), ctx, S), "narrow numBlocks")
 
 
+def test_scores_row_groups_span_sequences(qsa, O):
+    """A wide logits row (numBlocks = 32768, 128 slices of 256 blocks, so few row groups) over
+    many short sequences: each row group walks bands of several sequences in turn (the kbar
+    fragments are reloaded per sequence), lengths 0, 1, 4, 5 and ragged, a chunk that starts
+    and ends mid-band; every row against the oracle."""
+    rng = np.random.default_rng(227)
+    dt, B, S, nb = "bf16", 9, 600, 32768
+    q = W.to_bits(rng.standard_normal((B, S, 4, 128), dtype=np.float32), dt)
+    kb = W.to_bits(rng.standard_normal((B, 160, 128), dtype=np.float32), dt)
+    kbw = np.zeros((B, nb, 128), np.uint16)
+    kbw[:, :160] = kb
+    ctx = np.array([600, 0, 1, 4, 5, 333, 599, 17, 600], np.int32)
+    r0, n = 7, B * S - 20
+    print(f"[gpu] scores row groups over {B} sequences, nb={nb}", flush=True)
+    got = _gpu_scores(qsa, q, kbw, ctx, dt, r0, n, nb)
+    ref = O.scores(q, kbw, ctx, r0, n, dt)
+    check_logits(got, ref, _abs_bound(q, kbw, dt, r0 + np.arange(n), ctx, S), "row groups")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_scores_decode(qsa, O, dt):
     """Decode scores of one query token per sequence against V-tails that the oracle's K1b
