@@ -370,10 +370,12 @@ def select_leg(qsa, torch, wl, logits, steps, warmup, rowStart=SCORE_ROWS[0]):
         assert rc == 0, qsa.qsa_last_error()
     us = _time_stream(torch, call, steps, warmup)
     alg = select_alg(S, nb, rowStart, numRows)
+    blocks = int(np.minimum((np.arange(rowStart, rowStart + numRows) + 1) // 4, nb).sum())
     del out
     return {"workload": f"long prefill rows [{rowStart}, {rowStart + numRows}) x {nb} blocks",
             "entry": "qsa_index_topk_expand", "us_per_call": us, "alg_bytes": alg,
-            "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS}
+            "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS,
+            "blocks": blocks, "ps_per_block": us * 1e6 / blocks}
 
 
 def select_long_leg(qsa, torch, steps, warmup):
@@ -457,9 +459,35 @@ def select_decode_leg(qsa, torch, steps, warmup):
         assert rc == 0, qsa.qsa_last_error()
     us = _time_stream(torch, call, steps, warmup)
     alg = 4 * int(np.minimum(ctx // 4, mb)[ctx // 4 > 512].sum()) + 4 * qsa.INDEX_WIDTH * len(ctx)
+    blocks = int(np.minimum(ctx // 4, mb).sum())
     return {"workload": f"decode, B={len(ctx)}, context up to {int(ctx.max())}",
             "entry": "qsa_index_topk_expand_decode", "us_per_call": us, "alg_bytes": alg,
-            "GBps": alg / us / 1e3}
+            "GBps": alg / us / 1e3, "blocks": blocks, "ps_per_block": us * 1e6 / blocks}
+
+
+def select_decode_long_leg(qsa, torch, steps, warmup, maxBlocks):
+    """Decode top-512 selection + expand (qsa_index_topk_expand_decode) over long rows: 64
+    sequences of maxBlocks / 2 to maxBlocks complete blocks, scores-like logits.  Rows this
+    long are cut into chunks selected by workgroups of their own and then merged."""
+    import numpy as np
+    from sparse_attention_indexer_qsa_amd import workloads as W
+    ctx = W.decode_long_ctx(maxBlocks)
+    lg = torch.from_numpy(W.decode_logits(5, ctx, maxBlocks, styles=("scores",))).cuda()
+    c = torch.from_numpy(ctx).cuda()
+    out = torch.empty(len(ctx), qsa.INDEX_WIDTH, dtype=torch.int32, device="cuda")
+
+    def call(st):
+        rc = qsa.lib.qsa_index_topk_expand_decode(out.data_ptr(), lg.data_ptr(), c.data_ptr(),
+                                                  None, 0, len(ctx), maxBlocks, st)
+        assert rc == 0, qsa.qsa_last_error()
+    us = _time_stream(torch, call, steps, warmup)
+    blocks = int(np.minimum(ctx // 4, maxBlocks).sum())
+    alg = 4 * blocks + 4 * qsa.INDEX_WIDTH * len(ctx)
+    del lg
+    return {"workload": f"decode, B={len(ctx)}, rows of {maxBlocks // 2} to {maxBlocks} blocks",
+            "entry": "qsa_index_topk_expand_decode", "us_per_call": us, "alg_bytes": alg,
+            "GBps": alg / us / 1e3, "hbm_frac": alg / us / 1e3 / HBM_PEAK_GBPS,
+            "blocks": blocks, "ps_per_block": us * 1e6 / blocks}
 
 
 def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows=SCORE_ROWS[1]):
@@ -926,7 +954,7 @@ def main():
     if args.copy_calib:
         copy_calib()
 
-    scores = select = select_long = select_decode = scores_decode = None
+    scores = select = select_long = select_decode = scores_decode = select_decode_long = None
     if not args.no_scores:
         print("[bench] timing the block scores", file=sys.stderr, flush=True)
         logits, scores = scores_leg(qsa, torch, sets[0], wl, min(args.steps, 50),
@@ -938,6 +966,10 @@ def main():
               flush=True)
         select_long = select_long_leg(qsa, torch, min(args.steps, 50), min(args.warmup, 5))
         select_decode = select_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
+        print("[bench] timing the decode selection on long rows", file=sys.stderr, flush=True)
+        select_decode_long = [select_decode_long_leg(qsa, torch, min(args.steps, 50),
+                                                     min(args.warmup, 5), mb)
+                              for mb in (65536, 262144)]
         scores_decode = scores_decode_leg(qsa, torch, min(args.steps, 100), min(args.warmup, 10))
     decode = None
     if not args.no_decode:
@@ -989,6 +1021,7 @@ def main():
         "select_long_rows": select_long,
         "scores_decode": scores_decode,
         "select_decode": select_decode,
+        "select_decode_long_rows": select_decode_long,
         "configs": configs,
     }
     if not args.no_cpu:

@@ -480,7 +480,7 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
   if (splitCounters != nullptr) TRY(need(splitCounters, "splitCounters", 4));
   if (maxBlocks > QSA_TOPK) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(batchSize, 512));  // one 512-thread workgroup per sequence
+  TRY(check_grid(qsa::topk_decode_workgroups(batchSize, maxBlocks), 512));
   const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
                               splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
   TRY(device_ready());

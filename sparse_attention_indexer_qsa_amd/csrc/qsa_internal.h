@@ -141,6 +141,7 @@ struct TopkDecodeArgs {
   int32_t* splitCounters;  // nullable: [B, numKVHeads] zeroed
   int32_t numKVHeads;
   int32_t B, maxBlocks;
+  int32_t chunk = 0, numChunks = 0;  // split rows: set by the launcher
 };
 
 // Launchers: enqueue on `stream`, return the launch status.  Arguments are already validated.
@@ -153,6 +154,8 @@ hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream);
 // Workgroups of the prefill scores launch for a.S, a.numBlocks, a.rowStart, a.numRows (the
 // launcher fills the tile fields the same way), and its threads per workgroup.
 int64_t scores_workgroups(ScoresArgs& a);
+// Workgroups of the largest grid the decode selection launches for B sequences of maxBlocks.
+int64_t topk_decode_workgroups(int32_t B, int32_t maxBlocks);
 constexpr int kScoresThreads = 512;
 hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_ids_fill(int32_t* ids, int64_t total, int32_t numBlocks, hipStream_t stream);

@@ -37,13 +37,17 @@
 //    equal keys come out in ascending id and the first kSel are the result.  More than 1024
 //    such keys (many equal keys at T), or candidates too many for LDS after the first pass,
 //    take the ordered path below, then the same sort.
-//  * Decode: the selection is emitted in ascending id: one block scan per register group
-//    counts, for each key, the keys above T and the keys equal to T with smaller ids.
+//  * Decode: the selection is emitted in ascending id: the counts before each key of keys
+//    above T and of keys equal to T come from per-wave counts of each register group (one
+//    barrier) and ballots within the wave; each key writes its id to its rank in LDS (or to
+//    a spare slot when not taken), and the ranks are written out in order.
 //
 // Prefill rows longer than 18432 blocks take the one-wave-per-row kernel (a walk of the row
-// against a running threshold into an LDS candidate buffer, below).  Decode rows that long
-// take the streaming kernel at the end of the file (the same radix select with 8-bit digits
-// over the whole key range, the row re-read from L2 on every pass), 256 threads per row.
+// against a running threshold into an LDS candidate buffer, below).  Decode rows longer than
+// 32768 blocks (up to 262144) are cut into at most 8 chunks, each selected by a workgroup of
+// its own, and a second kernel merges the chunks' candidates (below); longer ones take the
+// streaming kernel at the end of the file (the same radix select with 8-bit digits over the
+// whole key range, the row re-read from L2 on every pass), 256 threads per row.
 
 #include <float.h>
 
@@ -83,12 +87,13 @@ __device__ __forceinline__ void write_tail_and_pad(int* out, int from, int64_t n
 struct RegShared {
   int hist[2][256];          // radix histograms, alternating between passes
   int wcnt[2][kMaxW];        // per-wave counts (double-buffered by caller's parity)
+  int gcnt[16 * kMaxW];      // ordered_select: per register group and wave, packed counts
   uint32_t red[2][kMaxW];    // per-wave max / min
   int found[2][2];           // per histogram buffer: chosen bin, keys above it
   uint32_t candU[kCandCap];
   int32_t candId[kCandCap];
   uint64_t sortBuf[2 * kTopK];
-  int32_t selId[kTopK];
+  int32_t selId[kTopK + 64];  // ordered_select: ranks kTopK.. take the unselected keys' writes
 };
 
 // Id of register key r of thread tid in a workgroup of NT threads.
@@ -382,43 +387,74 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
 }
 
 // The selected keys in ascending id (registers): above T, then the first `need` keys equal to
-// T (padding keys have the largest ids and are never among them).  emit(pos, id, u) receives
-// each selected key with its rank pos in ascending id.
-template <int NT, int KPT, class Emit>
+// T (padding keys have the largest ids and are never among them).  sh.selId[pos] receives
+// value(id, r) of the key of rank pos in ascending id (register index r), pos < kTopK.
+// Ids run group-major (register group g = r / 4 holds ids [4 NT g, 4 NT (g + 1))), then by
+// thread, then by the key's place in its group.  One barrier: each wave first publishes its
+// count of keys above T and equal to T per group; the counts before a key are then the sums
+// over earlier (group, wave) pairs, over lower lanes of its wave (ballots), and over its own
+// earlier keys of the group.  No branch per key: a key not selected writes to a slot of its
+// lane past kTopK.
+template <int NT, int KPT, class Value>
 __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_t T, int need,
-                                               RegShared& sh, Emit emit) {
-  const int tid = fresh_tid();
-  int aboveRun = 0, tieRun = 0;
+                                               RegShared& sh, Value value) {
+  constexpr int G = KPT / 4, W = NT / 64;
+  static_assert(G * W <= 128 && W % 2 == 0, "the count table holds 128 entries, 2 per lane");
+  const int tid = fresh_tid(), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  // counts of a group's keys above T (low 16 bits) and equal to T (high 16 bits) over the
+  // wave; block totals stay below 65536
 #pragma unroll
-  for (int g = 0; g < KPT / 4; ++g) {
-    // one group at a time: evaluated ahead, the comparisons of all groups would be held as
-    // lane masks across the scans
-    __builtin_amdgcn_sched_barrier(0);
+  for (int g = 0; g < G; ++g) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c += __popcll(__ballot(u[4 * g + e] > T));
+      c += __popcll(__ballot(u[4 * g + e] == T)) << 16;
+    }
+    if (lane == 0) sh.gcnt[g * W + wave] = c;
+  }
+  __syncthreads();
+  // exclusive prefix over the table in (group, wave) order: lane l holds entries 2l, 2l + 1
+  const int2 pr = lane < (G * W) / 2 ? reinterpret_cast<const int2*>(sh.gcnt)[lane]
+                                     : make_int2(0, 0);
+  const int pair = pr.x + pr.y;
+  int incl = pair;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const int exPair = incl - pair;
+  // T through an empty asm: the comparisons are made again per group rather than the first
+  // loop's lane masks held across the barrier (two SGPR pairs per key)
+  uint32_t T2 = T;
+  asm volatile("" : "+v"(T2));
+  const int dummy = kTopK + lane;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    // entry g * W + wave sits in lane (g * W + wave) / 2, as its second half for odd waves
+    const int src = (g * W + wave) >> 1;
+    int base = __builtin_amdgcn_readlane(exPair, src);
+    if (wave & 1) base += __builtin_amdgcn_readlane(pr.x, src);
     bool ab[4], ti[4];
-    int packed = 0;
+    int a = base & 0xFFFF, t = base >> 16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ab[e] = u[4 * g + e] > T2;
+      ti[e] = u[4 * g + e] == T2;
+      a += lanes_below(__ballot(ab[e]));
+      t += lanes_below(__ballot(ti[e]));
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e;
-      ab[e] = u[r] > T;
-      ti[e] = u[r] == T;
-      packed += (ab[e] ? 1 : 0) + (ti[e] ? 0x10000 : 0);
+      const int pos = a + (ab[e] ? (t < need ? t : need) : t);
+      const bool sel = (ab[e] || (ti[e] && t < need)) && pos < kTopK;
+      sh.selId[sel ? pos : dummy] = value(key_id<NT>(r, tid), r);
+      a += ab[e] ? 1 : 0;
+      t += ti[e] ? 1 : 0;
     }
-    int tot;
-    const int ex = block_excl_scan<NT>(packed, sh.wcnt[g & 1], &tot);
-    int a = aboveRun + (ex & 0xFFFF), t = tieRun + (ex >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g + e;
-      if (ab[e]) {
-        emit(a + (t < need ? t : need), key_id<NT>(r, tid), u[r]);
-        ++a;
-      } else if (ti[e]) {
-        if (t < need) emit(a + t, key_id<NT>(r, tid), u[r]);
-        ++t;
-      }
-    }
-    aboveRun += tot & 0xFFFF;
-    tieRun += tot >> 16;
   }
   __syncthreads();
 }
@@ -639,12 +675,108 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
     uint32_t u[KPT];
     load_keys<kDT, KPT, kVec>(row, n, u);
     const Threshold th = select_threshold<kDT, KPT>(u, n, kSel, sh);
-    ordered_select<kDT, KPT>(u, th.T, th.need, sh, [&](int pos, int id, uint32_t) {
-      if (pos < kTopK) {
+    // the selection gathers in LDS by rank and is written out in order, 4 tokens per block
+    ordered_select<kDT, KPT>(u, th.T, th.need, sh, [](int id, int) { return id; });
+    for (int s = tid; s < 4 * kSel; s += kDT) out[s] = 4 * sh.selId[s >> 2] + (s & 3);
+  }
+  write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kDT);
+}
+
+// ------------------------------------------------------------- decode, split rows ---
+//
+// Decode rows longer than one register-resident workgroup holds.  The row is cut into
+// numChunks chunks of `chunk` keys (a power of two, at most 32768; numChunks <= 8), one
+// workgroup per chunk.  The 512 largest keys of a chunk (u desc, id asc) include every key
+// of the row's 512 largest that lies in it: any other key of the chunk has 512 keys of its
+// own chunk ranking above it.  The chunk pass writes those keys' chunk-local ids (< 32768),
+// in ascending order, as 16-bit values into the sequence's own output row (512 per chunk;
+// the row's 8204 bytes hold the 4096 of 8 chunks); a chunk of at most 512 keys writes
+// nothing, all its keys being candidates.  The merge pass, one workgroup per sequence, reads
+// the candidates back (ascending id: chunk by chunk, each in ascending order), gathers their
+// keys from the row and selects among them exactly as the register kernel selects over a
+// row, into the same output row once every candidate is read.  Each key is read from HBM
+// once; the merge gathers at most 4096 keys of a sequence again.
+
+constexpr int kSplitMaxChunks = 8;
+constexpr int kSplitMaxChunk = kDT * 64;  // 32768 keys: 64 per thread
+
+template <int KPT, bool kVec>
+__global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(reg_waves(KPT))))
+void topk_decode_chunk_kernel(TopkDecodeArgs a) {
+  __shared__ RegShared sh;
+  const int64_t b = blockIdx.x / a.numChunks;
+  const int j = (int)(blockIdx.x % a.numChunks);
+  const int64_t c = a.ctx[b];
+  if (c <= 0) return;
+  const int64_t nVisC = c / 4;
+  const int n = (int)(nVisC < a.maxBlocks ? nVisC : a.maxBlocks);
+  const int nj = min(n - j * a.chunk, a.chunk);  // keys of this chunk (<= 0: none)
+  if (nj <= kTopK) return;                       // n <= 512 included
+  const float* row = a.logits + b * a.maxBlocks + (int64_t)j * a.chunk;
+  uint32_t u[KPT];
+  load_keys<kDT, KPT, kVec>(row, nj, u);
+  const Threshold th = select_threshold<kDT, KPT>(u, nj, kTopK, sh);
+  ordered_select<kDT, KPT>(u, th.T, th.need, sh, [](int id, int) { return id; });
+  // two ids a word: chunk j's 512 ids are bytes [1024 j, 1024 j + 1024) of the output row
+  uint32_t* st = reinterpret_cast<uint32_t*>(a.outIdx + b * kIndexWidth) + j * (kTopK / 2);
+  const int tid = threadIdx.x;
+  if (tid < kTopK / 2)
+    st[tid] = (uint32_t)sh.selId[2 * tid] | ((uint32_t)sh.selId[2 * tid + 1] << 16);
+}
+
+// KPT = 4 for up to 4 chunks (2048 candidate slots), 8 for up to 8.
+template <int KPT>
+__global__ __launch_bounds__(kDT) void topk_decode_merge_kernel(TopkDecodeArgs a) {
+  __shared__ RegShared sh;
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  int32_t* out = a.outIdx + b * kIndexWidth;
+  if (a.splitCounters != nullptr)
+    for (int h = tid; h < a.numKVHeads; h += kDT) a.splitCounters[b * a.numKVHeads + h] = 0;
+  const int64_t c = a.ctx[b];
+  if (c <= 0) {
+    for (int s = tid; s < kIndexWidth; s += kDT) out[s] = -1;
+    return;
+  }
+  const int64_t nVisC = c / 4;
+  const int n = (int)(nVisC < a.maxBlocks ? nVisC : a.maxBlocks);
+  const int kSel = n < kTopK ? n : kTopK;
+  if (n <= kTopK) {
+    for (int s = tid; s < 4 * n; s += kDT) out[s] = s;  // block s/4, token s%4
+  } else {
+    const int P = (n + a.chunk - 1) / a.chunk;         // chunks holding keys (<= numChunks)
+    const int last = n - (P - 1) * a.chunk;            // keys of the last of them
+    const int nCand = (P - 1) * kTopK + min(last, kTopK);
+    const float* row = a.logits + b * a.maxBlocks;
+    const uint32_t* st = reinterpret_cast<const uint32_t*>(out);  // two 16-bit ids a word
+    // slots s .. s + 3 of group g (slot = candidate index, in ascending id) lie in one chunk
+    uint32_t u[KPT];
+    int ids[KPT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[4 * pos + j] = 4 * id + j;
+    for (int g = 0; g < KPT / 4; ++g) {
+      const int s = (g * kDT + tid) * 4;
+      const int j = s / kTopK, k = s % kTopK;
+      const int nj = j < P - 1 ? a.chunk : last;
+      const uint32_t w0 = st[s / 2], w1 = st[s / 2 + 1];  // s / 2 + 1 < 2048 <= 2051 words
+      const int staged[4] = {(int)(w0 & 0xFFFFu), (int)(w0 >> 16), (int)(w1 & 0xFFFFu),
+                             (int)(w1 >> 16)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // a staged id is below nj by construction; the clamp keeps the gather inside the row
+        const int local = nj > kTopK ? min(staged[e], nj - 1) : k + e;
+        ids[4 * g + e] = s + e < nCand ? j * a.chunk + local : 0;
       }
-    });
+    }
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) u[r] = __float_as_uint(row[ids[r]]);
+#pragma unroll
+    for (int r = 0; r < KPT; ++r)
+      u[r] = key_id<kDT>(r, tid) < nCand ? orderable_bits(u[r]) : 0u;
+    // every staged id is read (the gathers use them): the row may be written from here on,
+    // once the barriers of the select have passed
+    const Threshold th = select_threshold<kDT, KPT>(u, nCand, kSel, sh);
+    ordered_select<kDT, KPT>(u, th.T, th.need, sh, [&](int, int r) { return ids[r]; });
+    for (int s = tid; s < 4 * kSel; s += kDT) out[s] = 4 * sh.selId[s >> 2] + (s & 3);
   }
   write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kDT);
 }
@@ -1252,11 +1384,55 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Chunk of the split decode selection for rows of maxBlocks keys (0: not split): the smallest
+// power of two from 4096 on that cuts a row into at most 8 chunks.
+static int split_chunk(int32_t maxBlocks) {
+  if (maxBlocks <= kDT * 64 || maxBlocks > kSplitMaxChunks * kSplitMaxChunk) return 0;
+  int chunk = 4096;
+  while ((int64_t)chunk * kSplitMaxChunks < maxBlocks) chunk *= 2;
+  return chunk;
+}
+
+int64_t topk_decode_workgroups(int32_t B, int32_t maxBlocks) {
+  const int chunk = split_chunk(maxBlocks);
+  return chunk ? (int64_t)B * ((maxBlocks + chunk - 1) / chunk) : B;
+}
+
+#define QSA_CHUNK_CASE(K, GRID, ARGS)                                                          \
+  case K:                                                                                      \
+    if (aligned)                                                                               \
+      hipLaunchKernelGGL((topk_decode_chunk_kernel<K, true>), GRID, dim3(kDT), 0, stream, ARGS); \
+    else                                                                                       \
+      hipLaunchKernelGGL((topk_decode_chunk_kernel<K, false>), GRID, dim3(kDT), 0, stream, ARGS); \
+    break;
+
+static hipError_t launch_split_decode(TopkDecodeArgs a, bool aligned, hipStream_t stream) {
+  a.chunk = split_chunk(a.maxBlocks);
+  a.numChunks = (a.maxBlocks + a.chunk - 1) / a.chunk;
+  const dim3 cgrid((unsigned)((int64_t)a.B * a.numChunks));
+  switch (a.chunk / kDT) {
+    QSA_CHUNK_CASE(8, cgrid, a)
+    QSA_CHUNK_CASE(16, cgrid, a)
+    QSA_CHUNK_CASE(32, cgrid, a)
+    default: QSA_CHUNK_CASE(64, cgrid, a)
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.numChunks <= 4)
+    hipLaunchKernelGGL(topk_decode_merge_kernel<4>, dim3((unsigned)a.B), dim3(kDT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(topk_decode_merge_kernel<8>, dim3((unsigned)a.B), dim3(kDT), 0, stream, a);
+  return hipGetLastError();
+}
+
+#undef QSA_CHUNK_CASE
+
 hipError_t launch_topk_expand_decode(const TopkDecodeArgs& a, hipStream_t stream) {
   const bool aligned = (a.maxBlocks & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
   const int kpt = keys_per_thread(a.maxBlocks, kDT);
   const dim3 grid((unsigned)a.B);
   if (kpt == 0) {
+    if (split_chunk(a.maxBlocks)) return launch_split_decode(a, aligned, stream);
     hipLaunchKernelGGL(topk_expand_decode_stream_kernel, grid, dim3(kSelThreads), 0, stream, a);
   } else {
     switch (kpt) {

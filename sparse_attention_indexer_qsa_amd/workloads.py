@@ -284,5 +284,13 @@ def decode_logits(seed, ctx, maxBlocks, styles=("scores", "ties", "normal", "spe
     return out
 
 
+def decode_long_ctx(maxBlocks, B=64, seed=41):
+    """Contexts of a decode batch over long sequences: B contexts uniform in [2 * maxBlocks,
+    4 * maxBlocks + 3], so that every sequence holds between maxBlocks / 2 and maxBlocks
+    complete blocks (128K to 256K tokens for maxBlocks = 65536, 512K to 1M for 262144)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(2 * maxBlocks, 4 * maxBlocks + 4, B).astype(np.int32)
+
+
 def make(n, **kw):
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)

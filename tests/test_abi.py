@@ -268,6 +268,13 @@ def test_next_rows_validation(qsa, host):
     assert tkd(B=-1) == E and tkd(mb=-1) == E and tkd(sc=h.p(4), H=-1) == E
     assert tkd(sc=h.p(4, 2), H=2) == A and tkd(out=None) == E and tkd(lg=None) == E
     assert tkd(B=2**23) == E                                  # 512-thread workgroups
+    # rows of more than 32768 blocks take one workgroup per chunk of up to 8 (8192 to 32768
+    # keys each): the grid is batchSize * chunks (valid calls: no device here, no launch)
+    ND = qsa.QSA_E_NO_DEVICE
+    assert tkd(B=2**20 - 1, mb=65536) == ND                   # 8 chunks: 2^23 - 8 workgroups
+    assert tkd(B=2**20, mb=65536) == E
+    assert tkd(B=2**21, mb=32772) == E                        # 5 chunks of 8192
+    assert tkd(B=2**21 - 1, mb=262145) == ND                  # longer rows: one per sequence
     assert tkd(mb=512, lg=None) != E                          # nVis <= 512 reads no logits
     assert tkd(B=0, out=None) == OK
 

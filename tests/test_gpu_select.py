@@ -257,6 +257,57 @@ def test_topk_expand_decode_bench_batch(qsa, O):
     print(f"[parity] topk_expand_decode bench batch: {len(ctx)} rows bit-exact", flush=True)
 
 
+# Rows cut into chunks (maxBlocks above 32768): chunk lengths 8192, 16384 and 32768 occur.
+SPLIT_CASES = [(32772, 64), (65536, 64), (131071, 32), (200001, 24), (262144, 64)]
+
+
+@pytest.mark.parametrize("maxBlocks,B", SPLIT_CASES)
+def test_topk_expand_decode_long_rows(qsa, O, maxBlocks, B):
+    """Long decode rows: contexts around every chunk boundary a row of these lengths can have
+    (a chunk of 1, 512 and 513 keys, a row ending on a boundary), ctx <= 0, rows of <= 512
+    blocks, capped contexts, and all four logit styles (ties spread across chunks, -inf, NaNs
+    of both signs); aligned and unaligned rows."""
+    rng = np.random.default_rng(11 + maxBlocks)
+    ctx = rng.integers(1, 4 * maxBlocks + 40, B).astype(np.int32)
+    special = [0, -5, 2048, 2052, 4 * maxBlocks + 3, 1]
+    for c in (8192, 16384, 32768):
+        for n in (c - 1, c, c + 1, c + 512, c + 513, 2 * c + 7, 7 * c + 300):
+            if n <= maxBlocks:
+                special.append(4 * n + int(rng.integers(0, 4)))
+    special = special[:B]
+    ctx[:len(special)] = special
+    logits = W.decode_logits(17, ctx, maxBlocks)
+    ref, ref_sc = O.topk_expand_decode(logits, ctx, np.full((B, 3), 9, np.int32))
+    out = G.Guarded((B, WIDTH), torch.int32, fill=POISON)
+    sc = G.Guarded((B, 3), torch.int32, fill=9)
+    print(f"[gpu] topk_expand_decode long rows maxBlocks={maxBlocks} B={B}", flush=True)
+    qsa.qsa_index_topk_expand_decode(out.t, G.dev(logits), G.dev(ctx), maxBlocks,
+                                     splitCounters=sc.t, numKVHeads=3)
+    got = _host(out)
+    assert np.array_equal(_host(sc), ref_sc)
+    bad = np.flatnonzero(np.any(got != ref, axis=1))
+    assert bad.size == 0, f"{bad.size} sequences differ, first {bad[0]} (ctx {ctx[bad[0]]})"
+    print(f"[parity] topk_expand_decode long rows maxBlocks={maxBlocks}: {B} rows bit-exact",
+          flush=True)
+
+
+@pytest.mark.parametrize("maxBlocks", [65536, 262144])
+def test_topk_expand_decode_long_bench_batch(qsa, O, maxBlocks):
+    """The launches the benchmark times for long decode rows: 64 sequences of maxBlocks / 2 to
+    maxBlocks complete blocks, scores-like logits."""
+    ctx = W.decode_long_ctx(maxBlocks)
+    logits = W.decode_logits(5, ctx, maxBlocks, styles=("scores",))
+    ref = O.topk_expand_decode(logits, ctx)
+    out = G.Guarded((len(ctx), WIDTH), torch.int32, fill=POISON)
+    print(f"[gpu] topk_expand_decode long bench batch maxBlocks={maxBlocks}", flush=True)
+    qsa.qsa_index_topk_expand_decode(out.t, G.dev(logits), G.dev(ctx), maxBlocks)
+    got = _host(out)
+    bad = np.flatnonzero(np.any(got != ref, axis=1))
+    assert bad.size == 0, f"{bad.size} sequences differ, first {bad[0]} (ctx {ctx[bad[0]]})"
+    print(f"[parity] topk_expand_decode long bench batch maxBlocks={maxBlocks}: "
+          f"{len(ctx)} rows bit-exact", flush=True)
+
+
 def test_topk_expand_decode_all_ones_nan(qsa, O):
     """Decode rows holding FP32 bits 0xFFFFFFFF (the smallest key): all of them (threshold 0,
     padding keys equal to it), one register group of them inside ordinary values, and a few
