@@ -251,8 +251,8 @@ int qsa_index_scores(float* logits, const void* qNormed, const void* kbar,
  * qNormed  [in]  T [B, 1, 4, 128] (one query token per sequence).
  * contextLengths [in] device int32 [B]: TOTAL lengths.   pool: required (kbar is read from the
  * V-tail of token 4g).  Same score as qsa_index_scores; a block whose V page entry is unused
- * or out of range scores -FLT_MAX.  maxBlocks <= 65535*64.  Grid (B, ceil(maxBlocks/64)) of
- * 256-thread workgroups; a batch larger than one launch holds is rejected (QSA_E_INVALID).
+ * or out of range scores -FLT_MAX.  B * ceil(maxBlocks / 128) workgroups of 64 threads; a
+ * batch larger than one launch holds (more than 2^26 - 1 of them) is rejected (QSA_E_INVALID).
  */
 int qsa_index_scores_decode(float* logits, const void* qNormed, const int32_t* contextLengths,
                             const qsa_pool_state_t* pool, int32_t batchSize, int32_t maxBlocks,

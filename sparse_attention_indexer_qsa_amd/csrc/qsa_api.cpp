@@ -386,14 +386,12 @@ QSA_EXPORT int qsa_index_scores_decode(float* logits, const void* qNormed,
   if (batchSize < 0 || maxBlocks < 0)
     return fail(QSA_E_INVALID, "batchSize = %d, maxBlocks = %d", batchSize, maxBlocks);
   if (batchSize == 0 || maxBlocks == 0) return ok();
-  if ((maxBlocks + 63) / 64 > 65535)
-    return fail(QSA_E_INVALID, "maxBlocks = %d exceeds the supported %d", maxBlocks, 65535 * 64);
   TRY(need(logits, "logits", 4));
   TRY(need(qNormed, "qNormed", 16));
   TRY(need(contextLengths, "contextLengths", 4));
   qsa::PoolArgs p{};
   TRY(check_pool(pool, &p));
-  TRY(check_grid(batchSize));  // grid (batchSize, ceil(maxBlocks / 64))
+  TRY(check_grid(qsa::scores_decode_workgroups(batchSize, maxBlocks), 64));
   const qsa::ScoresDecodeArgs a{logits, qNormed, contextLengths, p, batchSize, maxBlocks};
   TRY(device_ready());
   (void)hipGetLastError();

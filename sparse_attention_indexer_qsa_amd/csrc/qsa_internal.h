@@ -154,6 +154,8 @@ hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream);
 // Workgroups of the prefill scores launch for a.S, a.numBlocks, a.rowStart, a.numRows (the
 // launcher fills the tile fields the same way), and its threads per workgroup.
 int64_t scores_workgroups(ScoresArgs& a);
+// Workgroups (64 threads) of the decode scores launch for B sequences of maxBlocks blocks.
+int64_t scores_decode_workgroups(int32_t B, int32_t maxBlocks);
 // Workgroups of the largest grid the decode selection launches for B sequences of maxBlocks.
 int64_t topk_decode_workgroups(int32_t B, int32_t maxBlocks);
 constexpr int kScoresThreads = 512;

@@ -27,8 +27,8 @@
 //    workgroup can see skip the contraction and store -FLT_MAX.  The kernel is bound by the
 //    FP32 logits it writes.
 //
-// Decode gathers kbar rows from the paged pool (one 16-lane DPP row per block, the 4+4 dims
-// split of qsa_device.h), four FP32 dot products per block reduced by DPP, on the VALU.
+// Decode gathers kbar rows from the paged pool and scores them on MFMA too (16x16x32, the
+// sequence's four heads as the A rows): the kernel is bound by those gathers.
 
 #include <float.h>
 
@@ -244,82 +244,95 @@ void scores_kernel(ScoresArgs a) {
   }
 }
 
-// Decode: grid (B, ceil(maxBlocks / kDecBlocks)); DPP row R = 4*wave + r of a workgroup takes
-// blocks g = kDecBlocks*blockIdx.y + R + 16*k, k < kDecK.  q of the sequence is held by every
-// row (4 heads x the lane's 8 dims).
-constexpr int kDecK = 4;                 // blocks per DPP row (8 measured slower)
-constexpr int kDecBlocks = 16 * kDecK;   // blocks per workgroup
+// Decode on MFMA (v_mfma_f32_16x16x32): one wave per workgroup takes kDecGroups groups of
+// 16 consecutive blocks, 16-aligned, so that a group's 64 tokens lie in one 128-token page:
+// one page-table entry per group (a scalar load), issued for every group before anything
+// else.  The sequence's q is the A operand (rows 0..3 = heads, rows 4..15 zero), the group's
+// 16 gathered kbar rows the B operand: for k-step s lane l holds the 8 dims
+// [8 (l / 16) + 32 s, +8) of block l % 16 (A: the same dims of head l % 16), so that the four
+// lanes of a block read 64 contiguous bytes per load.  Lane l < 16 of the accumulator holds
+// the four heads of block l % 16: ReLU, the ascending head sum and the scale there.
+// Workgroup w takes chunk w % nChunks of sequence w / nChunks: consecutive workgroups, which
+// the dispatcher spreads over the XCDs in turn, cover consecutive chunks of one sequence, so
+// every XCD gets a share of every sequence (sequence-major placement left one XCD with 22 %
+// more blocks than the mean on the decode batch, and the time followed it).  Measured on the
+// 64-sequence decode batch (77 MB): 14.9 us, against 20.3 us for the earlier VALU kernel
+// (DPP-row dot products, 256-thread workgroups, sequence-major); the VALU kernel with this
+// placement took 17.7 us, MFMA workgroups of 4 waves 18.3 us.
+constexpr int kDecGroups = 8;                    // 16-block groups per workgroup (6: 15.2 us,
+                                                 // 12: 15.2 us, 16: spills)
+constexpr int kDecBlocks = 16 * kDecGroups;      // blocks per workgroup
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(Bf16, const uint4& a, const uint4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(F16, const uint4& a, const uint4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void scores_decode_kernel(ScoresDecodeArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane >> 4, c = lane & 15;
-  const int64_t b = blockIdx.x;
-  const int64_t gBase = kDecBlocks * (int64_t)blockIdx.y;
-  // The page-table entries of the row's kDecK blocks and the sequence's q depend on the block
-  // index alone: they are loaded before the context length is known, and the V-tail addresses
-  // depend on the entries alone (a block past the context, or behind an entry that fails a
-  // guard of tail_offset -- slot in range, entry not -1 and inside the pool -- reads page 0's
-  // row, unused), so the dependent latencies are the entry's and the V-tail's.
+__global__ __launch_bounds__(64) void scores_decode_kernel(ScoresDecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int n = lane & 15, kq = lane >> 4;  // block of the group; 8-dim slice of each k-step
+  const int nChunks = (a.maxBlocks + kDecBlocks - 1) / kDecBlocks;
+  const int64_t b = blockIdx.x / nChunks;
+  const int64_t g0 = (int64_t)kDecBlocks * (blockIdx.x % nChunks);
   const int32_t* vt = a.pool.pageTable + (b * 2 + 1) * a.pool.maxPagesPerSeq;
-  int32_t id[kDecK];
+  // The page-table entries and q depend on the block index alone: issued before the context
+  // length is known (a memory clobber keeps them ahead of the early return)
+  int32_t id[kDecGroups];
 #pragma unroll
-  for (int k = 0; k < kDecK; ++k) {
-    const int64_t slot = (4 * (gBase + 4 * wave + r + 16 * k)) >> 7;
+  for (int k = 0; k < kDecGroups; ++k) {
+    const int64_t slot = (g0 + 16 * k) >> 5;  // page slot of tokens 4 (g0 + 16k) .. + 63
     id[k] = vt[slot < a.pool.maxPagesPerSeq ? slot : a.pool.maxPagesPerSeq - 1];
   }
-  Piece qp[4];
+  uint4 qa[4];
+  const uint16_t* qrow =
+      static_cast<const uint16_t*>(a.qNormed) + (b * 4 + (n & 3)) * kDim + 8 * kq;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) qp[h] = load_piece(a.qNormed, (b * 4 + h) * kDim, c);
-  // a memory clobber: the loads above are issued here, not sunk past the early return below
+  for (int s = 0; s < 4; ++s) qa[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
   asm volatile("" ::: "memory");
   const int64_t ctx = a.ctx[b];
   int64_t nVis = ctx > 0 ? ctx / 4 : 0;
   if (nVis > a.maxBlocks) nVis = a.maxBlocks;
-  if (gBase >= nVis) return;
-  int64_t off[kDecK];
-  bool okT[kDecK];
+  if (g0 >= nVis) return;
 #pragma unroll
-  for (int k = 0; k < kDecK; ++k) {
-    const int64_t g = gBase + 4 * wave + r + 16 * k, pos = 4 * g;
-    okT[k] = ((pos >> 7) < a.pool.maxPagesPerSeq) & (id[k] >= 0) & (id[k] < a.pool.numIds);
-    const int64_t o = ((int64_t)(okT[k] ? id[k] : 0) * kPageTokens + (pos & (kPageTokens - 1))) *
-                          a.pool.rowElems + a.pool.headSize;
-    off[k] = okT[k] ? o : 0;
-  }
-  Piece kp[kDecK];
+  for (int s = 0; s < 4; ++s)
+    if (n >= 4) qa[s] = make_uint4(0u, 0u, 0u, 0u);
+  // V-tail rows: a group behind an entry that fails a guard of tail_offset (slot in range,
+  // entry not -1 and inside the pool) reads page 0's rows and scores -FLT_MAX; rows of blocks
+  // past the context are read from their page (inside the pool) and not stored
+  bool ok[kDecGroups];
+  uint4 kv[kDecGroups][4];
 #pragma unroll
-  for (int k = 0; k < kDecK; ++k) kp[k] = load_piece(a.pool.base, off[k], c);
-  float qa[4][4], qb[4][4];
+  for (int k = 0; k < kDecGroups; ++k) {
+    const int64_t g = g0 + 16 * k, slot = g >> 5;
+    ok[k] = (slot < a.pool.maxPagesPerSeq) & (id[k] >= 0) & (id[k] < a.pool.numIds);
+    const int64_t row =
+        (int64_t)(ok[k] ? id[k] : 0) * kPageTokens + ((4 * (g + n)) & (kPageTokens - 1));
+    const uint16_t* p = static_cast<const uint16_t*>(a.pool.base) + row * a.pool.rowElems +
+                        a.pool.headSize + 8 * kq;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    widen4(T{}, qp[h].a, qa[h]);
-    widen4(T{}, qp[h].b, qb[h]);
+    for (int s = 0; s < 4; ++s) kv[k][s] = *reinterpret_cast<const uint4*>(p + 32 * s);
   }
   const float scale = score_scale();
 #pragma unroll
-  for (int k = 0; k < kDecK; ++k) {
-    const int64_t g = gBase + 4 * wave + r + 16 * k;
+  for (int k = 0; k < kDecGroups; ++k) {
+    const int64_t g = g0 + 16 * k;
     if (g >= nVis) break;
-    if (!okT[k]) {  // unused or out-of-range V page entry
-      if (c == 0) a.logits[b * a.maxBlocks + g] = -FLT_MAX;
-      continue;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma16(T{}, qa[s], kv[k][s], acc);
+    if (lane < 16 && g + n < nVis) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) sum = sum + __builtin_fmaxf(acc[h], 0.0f);
+      a.logits[b * a.maxBlocks + g + n] = ok[k] ? scale * sum : -FLT_MAX;
     }
-    float ka[4], kb[4];
-    widen4(T{}, kp[k].a, ka);
-    widen4(T{}, kp[k].b, kb);
-    float s = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float d = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) d = __builtin_fmaf(qa[h][e], ka[e], d);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) d = __builtin_fmaf(qb[h][e], kb[e], d);
-      d = row_sum16(d);
-      s = s + __builtin_fmaxf(d, 0.0f);
-    }
-    if (c == 0) a.logits[b * a.maxBlocks + g] = scale * s;
   }
 }
 
@@ -343,11 +356,15 @@ hipError_t launch_scores(const ScoresArgs& a, Dt dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int64_t scores_decode_workgroups(int32_t B, int32_t maxBlocks) {
+  return (int64_t)B * ((maxBlocks + kDecBlocks - 1) / kDecBlocks);
+}
+
 hipError_t launch_scores_decode(const ScoresDecodeArgs& a, Dt dt, hipStream_t stream) {
-  const dim3 grid((unsigned)a.B, (unsigned)((a.maxBlocks + kDecBlocks - 1) / kDecBlocks));
+  const dim3 grid((unsigned)scores_decode_workgroups(a.B, a.maxBlocks));
   if (dt == Dt::BF16)
-    hipLaunchKernelGGL((scores_decode_kernel<Bf16>), grid, dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((scores_decode_kernel<F16>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((scores_decode_kernel<Bf16>), grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL((scores_decode_kernel<F16>), grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

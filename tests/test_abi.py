@@ -232,9 +232,11 @@ def test_next_rows_validation(qsa, host):
         a.update(kw)
         return L.qsa_index_scores_decode(a["lg"], a["q"], a["ctx"], a["pool"], a["B"], a["mb"],
                                          a["dt"], None)
-    assert scd(dt=9) == D and scd(B=-1) == E and scd(mb=-1) == E and scd(mb=65535 * 64 + 1) == E
+    assert scd(dt=9) == D and scd(B=-1) == E and scd(mb=-1) == E
+    # B * ceil(maxBlocks / 128) workgroups of 64 threads, at most 2^26 - 1
+    assert scd(B=2**19, mb=2**14 + 1) == E and scd(B=2**19 - 1, mb=2**14) != E
     assert scd(lg=None) == E and scd(q=h.p(1, 2)) == A and scd(pool=None) == E
-    assert scd(B=2**24) == E and scd(B=0, pool=None) == OK and scd(mb=0, lg=None) == OK
+    assert scd(B=2**26) == E and scd(B=0, pool=None) == OK and scd(mb=0, lg=None) == OK
 
     assert L.qsa_index_ids_fill(None, 4, 16, None) == E
     assert L.qsa_index_ids_fill(h.p(0, 2), 4, 16, None) == A
