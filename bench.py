@@ -590,11 +590,13 @@ def _counter(d, name):
 PROFILE_MD = os.path.join(ROOT, "profiles", "prefill_kernel_long_prefill.md")
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/ptrace -o run -- "
-             "python3 $R/bench.py --steps 50 --warmup 10 --no-cpu",
+             "python3 $R/bench.py --steps 50 --warmup 10 --no-cpu --no-configs",
     "fetch": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/pfetch -o run "
-             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode "
+             "--no-configs --copy-calib",
     "write": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/pwrite -o run "
-             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode --copy-calib",
+             "-- python3 $R/bench.py --steps 10 --warmup 2 --no-cpu --no-three-call --no-decode "
+             "--no-configs --copy-calib",
 }
 
 
@@ -618,6 +620,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     f_k, w_k = pick(fetch, "prefill_kernel"), pick(write, "prefill_kernel")
     fb, wb = f_k * 1024 * f_scale, w_k * 1024 * w_scale
     alg = algorithmic_bytes(W.config3())
+    alg_path = path_bytes(W.config3())
     rec = {"kernel": "prefill_kernel<Bf16, pool> on the long-prefill workload",
            "kernel_source_sha256_16": kernel_source_hash(), "fetch_bytes_per_launch": fb,
            "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
@@ -638,8 +641,12 @@ def summarize(trace_dir, fetch_dir, write_dir):
         name = r["Name"].replace("qsa::(anonymous namespace)::", "").split("(")[0]
         md.append(f"| `{name[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    md += ["", f"Fused kernel: {alg:,} B / {avg_us:.2f} us = {alg / avg_us / 1e6:.2f} TB/s = "
-           f"{100 * alg / avg_us / 1e6 / 8:.1f} % of the 8 TB/s HBM peak.", "",
+    md += ["", f"Fused kernel, on the path's algorithmic bytes (the three-call count, which "
+           f"charges the block positions' cosSin rows once per consuming call): {alg_path:,} B / "
+           f"{avg_us:.2f} us = {alg_path / avg_us / 1e6:.2f} TB/s = "
+           f"{100 * alg_path / avg_us / 1e6 / 8:.1f} % of the 8 TB/s HBM peak.",
+           f"On the bytes the fused launch itself must move: {alg:,} B / {avg_us:.2f} us = "
+           f"{alg / avg_us / 1e6:.2f} TB/s = {100 * alg / avg_us / 1e6 / 8:.1f} %.", "",
            "## HBM traffic (counters)", "",
            "One counter per run; each run includes `torch.mul` over 256 MiB of float32, a "
            "reference kernel that reads and writes 268,435,456 B:", "",
@@ -697,9 +704,50 @@ def summarize_next(stats, fetch, write, f_scale, w_scale):
             rel = f"{100 * (mb - alg) / alg:+.1f} %"
         md.append(f"| {label} | {us:.1f} | {alg:,} | {alg / us / 1e6:.2f} TB/s | "
                   f"{100 * alg / us / 1e6 / 8:.1f} | {meas} | {rel} |")
+    # decode kernels: the 64-sequence decode batch and the long-row decode batches
+    import numpy as np
+    from sparse_attention_indexer_qsa_amd import workloads as W
+    wl4 = W.config4()
+    dctx = (wl4.ranges[0] + 1).astype(np.int64)
+    dmb = int((dctx.max() + 3) // 4)
+    dn = np.minimum(dctx // 4, dmb)
+    dec = [("scores_decode_kernel", "`scores_decode_kernel<Bf16>` (qsa_index_scores_decode, "
+            "decode batch: 64 sequences, contexts up to 32772)", 260 * int(dn.sum()) + 1024 * 64),
+           ("topk_expand_decode_reg_kernel", "`topk_expand_decode_reg_kernel` "
+            "(qsa_index_topk_expand_decode, the same batch)",
+            4 * int(dn[dn > 512].sum()) + 4 * 2051 * 64)]
+    for mb, kpt in ((65536, 16), (262144, 64)):
+        c = W.decode_long_ctx(mb).astype(np.int64)
+        n = np.minimum(c // 4, mb)
+        dec.append((f"topk_decode_chunk_kernel<{kpt}", f"`topk_decode_chunk_kernel<{kpt}>` "
+                    f"(qsa_index_topk_expand_decode, 64 rows of {mb // 2} to {mb} blocks: "
+                    f"chunk pass; the 16-bit candidate ids it stages are not counted)",
+                    4 * int(n.sum())))
+    dec.append(("topk_decode_merge_kernel", "`topk_decode_merge_kernel<8>` (merge pass of both "
+                "long-row batches; its bytes: the staged ids, the candidates' keys and the "
+                "8204-byte rows, not counted above)", None))
+    md += ["", "## Decode kernels", "",
+           "| kernel | calls | avg us | algorithmic bytes | achieved | % of 8 TB/s | measured "
+           "bytes (fetch + write) |", "|---|---|---|---|---|---|---|"]
+    for key, label, alg in dec:
+        rows = [r for r in stats if key in r["Name"]]
+        if not rows:
+            continue
+        us = float(rows[0]["AverageNs"]) / 1e3
+        fk = [v for k, v in fetch.items() if key in k]
+        wk = [v for k, v in write.items() if key in k]
+        meas = "—"
+        if fk and wk:
+            mb_ = fk[0][0] * 1024 * f_scale + wk[0][0] * 1024 * w_scale
+            meas = f"{mb_:,.0f} ({fk[0][0] * 1024 * f_scale:,.0f} + {wk[0][0] * 1024 * w_scale:,.0f})"
+        ach = "—" if alg is None else f"{alg / us / 1e6:.2f} TB/s"
+        frac = "—" if alg is None else f"{100 * alg / us / 1e6 / 8:.1f}"
+        md.append(f"| {label} | {rows[0]['Calls']} | {us:.2f} | "
+                  f"{'—' if alg is None else f'{alg:,}'} | {ach} | {frac} | {meas} |")
     md += ["", "Algorithmic bytes: scores = 4 B per (row, block) logit written + 1024 B of q per "
            "row + 256 B per kbar row any row sees; selection = 4 B per complete-block logit read "
-           "+ 4 x 2051 B of token slots per row.", "",
+           "+ 4 x 2051 B of token slots per row; decode scores = 256 B of V-tail read + 4 B "
+           "written per visible block + 1024 B of q per sequence.", "",
            "Written by `python bench.py --summarize $OUT/ptrace $OUT/pfetch $OUT/pwrite`"
            "."]
     open(NEXT_MD, "w").write("\n".join(md) + "\n")
