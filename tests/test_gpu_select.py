@@ -257,8 +257,10 @@ def test_topk_expand_decode_bench_batch(qsa, O):
     print(f"[parity] topk_expand_decode bench batch: {len(ctx)} rows bit-exact", flush=True)
 
 
-# Rows cut into chunks (maxBlocks above 32768): chunk lengths 8192, 16384 and 32768 occur.
-SPLIT_CASES = [(32772, 64), (65536, 64), (131071, 32), (200001, 24), (262144, 64)]
+# Rows cut into chunks (maxBlocks above 32768): chunk lengths 8192, 16384 and 32768 occur;
+# rows above 262144 blocks take the streaming kernel (the last two cases).
+SPLIT_CASES = [(32772, 64), (65536, 64), (131071, 32), (200001, 24), (262144, 64),
+               (262148, 8), (300001, 8)]
 
 
 @pytest.mark.parametrize("maxBlocks,B", SPLIT_CASES)
