@@ -685,7 +685,7 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
 // ------------------------------------------------------------- decode, split rows ---
 //
 // Decode rows longer than one register-resident workgroup holds.  The row is cut into
-// numChunks chunks of `chunk` keys (a power of two, at most 32768; numChunks <= 8), one
+// numChunks chunks of `chunk` keys (8192, 16384 or 32768; 5 to 8 of them), one
 // workgroup per chunk.  The 512 largest keys of a chunk (u desc, id asc) include every key
 // of the row's 512 largest that lies in it: any other key of the chunk has 512 keys of its
 // own chunk ranking above it.  The chunk pass writes those keys' chunk-local ids (< 32768),
@@ -724,9 +724,10 @@ void topk_decode_chunk_kernel(TopkDecodeArgs a) {
     st[tid] = (uint32_t)sh.selId[2 * tid] | ((uint32_t)sh.selId[2 * tid + 1] << 16);
 }
 
-// KPT = 4 for up to 4 chunks (2048 candidate slots), 8 for up to 8.
-template <int KPT>
+// 8 keys per thread: 4096 candidate slots, the 512 of each of up to 8 chunks (a split row has
+// 5 to 8 chunks: the chunk is the smallest length that leaves at most 8).
 __global__ __launch_bounds__(kDT) void topk_decode_merge_kernel(TopkDecodeArgs a) {
+  constexpr int KPT = 8;
   __shared__ RegShared sh;
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -1385,10 +1386,10 @@ hipError_t launch_topk_expand(const TopkArgs& a, hipStream_t stream) {
 }
 
 // Chunk of the split decode selection for rows of maxBlocks keys (0: not split): the smallest
-// power of two from 4096 on that cuts a row into at most 8 chunks.
+// of 8192, 16384 and 32768 that cuts a row into at most 8 chunks (so 5 to 8 of them).
 static int split_chunk(int32_t maxBlocks) {
   if (maxBlocks <= kDT * 64 || maxBlocks > kSplitMaxChunks * kSplitMaxChunk) return 0;
-  int chunk = 4096;
+  int chunk = 8192;
   while ((int64_t)chunk * kSplitMaxChunks < maxBlocks) chunk *= 2;
   return chunk;
 }
@@ -1411,17 +1412,13 @@ static hipError_t launch_split_decode(TopkDecodeArgs a, bool aligned, hipStream_
   a.numChunks = (a.maxBlocks + a.chunk - 1) / a.chunk;
   const dim3 cgrid((unsigned)((int64_t)a.B * a.numChunks));
   switch (a.chunk / kDT) {
-    QSA_CHUNK_CASE(8, cgrid, a)
     QSA_CHUNK_CASE(16, cgrid, a)
     QSA_CHUNK_CASE(32, cgrid, a)
     default: QSA_CHUNK_CASE(64, cgrid, a)
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.numChunks <= 4)
-    hipLaunchKernelGGL(topk_decode_merge_kernel<4>, dim3((unsigned)a.B), dim3(kDT), 0, stream, a);
-  else
-    hipLaunchKernelGGL(topk_decode_merge_kernel<8>, dim3((unsigned)a.B), dim3(kDT), 0, stream, a);
+  hipLaunchKernelGGL(topk_decode_merge_kernel, dim3((unsigned)a.B), dim3(kDT), 0, stream, a);
   return hipGetLastError();
 }
 
