@@ -142,3 +142,45 @@ def test_decode_graph_replays_match_eager_calls():
                               ref):
             assert torch.equal(a, b), f"replay {seed}: {name} differs from the eager calls"
         print(f"[parity] decode graph replay {seed}: all outputs equal the eager calls", flush=True)
+
+
+def test_split_decode_selection_graph_replays():
+    """The decode selection of rows past 32768 blocks (a chunk launch that stages candidates in
+    the output rows, then a merge launch) captured once and replayed on fresh logits: every
+    replay equals an eager call, and the output rows hold no staging left over."""
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import sparse_attention_indexer_qsa_amd.qsa as qsa
+    mb, B = 65536, 16
+    ctx_np = W.decode_long_ctx(mb, B=B, seed=5)
+    ctx_np[:3] = [0, 2051, 4 * mb + 2]
+    ctx = G.dev(ctx_np)
+    logits = G.dev(W.decode_logits(21, ctx_np, mb))
+    out = torch.empty(B, qsa.INDEX_WIDTH, dtype=torch.int32, device="cuda")
+    sc = torch.empty(B, 3, dtype=torch.int32, device="cuda")
+
+    def step():
+        qsa.qsa_index_topk_expand_decode(out, logits, ctx, mb, splitCounters=sc, numKVHeads=3)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    print("[gpu] capturing the split decode selection", flush=True)
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for seed in (31, 32, 33):
+        logits.copy_(G.dev(W.decode_logits(seed, ctx_np, mb, styles=("scores", "ties"))))
+        step()
+        torch.cuda.synchronize()
+        ref = [out.clone(), sc.clone()]
+        out.fill_(-7)
+        sc.fill_(5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(sc, ref[1]), f"replay {seed}"
+        assert torch.all(sc == 0)
+    print("[parity] split decode selection: 3 graph replays equal eager calls", flush=True)
