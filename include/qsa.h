@@ -309,9 +309,10 @@ int qsa_index_topk_expand(int32_t* outIdx, const float* logits, const int32_t* c
  * One 512-thread workgroup per sequence; for maxBlocks in (32768, 262144] each row is cut
  * into c = ceil(maxBlocks / chunk) <= 8 chunks (chunk a power of two from 8192 to 32768),
  * selected by one workgroup each, and a second launch merges them: the chunk pass stages
- * 16-bit candidate ids in the sequence's own outIdx row, which the merge then overwrites
- * (outIdx therefore must not alias logits).  batchSize * c <= 2^23 - 1 (c = 1 for shorter
- * rows), else QSA_E_INVALID.  Rows above 262144 blocks take a kernel that re-reads the row.
+ * 16-bit candidate ids in the sequence's own outIdx row, which the merge then overwrites, so
+ * outIdx must not overlap logits (QSA_E_INVALID).  batchSize * c <= 2^23 - 1 (c = 1 for
+ * shorter rows), else QSA_E_INVALID.  Rows above 262144 blocks take a kernel that re-reads
+ * the row.
  */
 int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits,
                                  const int32_t* contextLengths, int32_t* splitCounters,

@@ -478,7 +478,17 @@ QSA_EXPORT int qsa_index_topk_expand_decode(int32_t* outIdx, const float* logits
   if (splitCounters != nullptr) TRY(need(splitCounters, "splitCounters", 4));
   if (maxBlocks > QSA_TOPK) TRY(need(logits, "logits", 4));
   TRY(need(contextLengths, "contextLengths", 4));
-  TRY(check_grid(qsa::topk_decode_workgroups(batchSize, maxBlocks), 512));
+  const int64_t wgs = qsa::topk_decode_workgroups(batchSize, maxBlocks);
+  TRY(check_grid(wgs, 512));
+  if (wgs > batchSize) {
+    // rows cut into chunks stage candidates in outIdx while logits are still being read
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(outIdx), l0 = reinterpret_cast<uintptr_t>(logits);
+    const uintptr_t o1 = o0 + (uintptr_t)batchSize * QSA_INDEX_WIDTH * 4;
+    const uintptr_t l1 = l0 + (uintptr_t)batchSize * (uintptr_t)maxBlocks * 4;
+    if (o0 < l1 && l0 < o1)
+      return fail(QSA_E_INVALID, "outIdx overlaps logits (rows of %d blocks are selected in "
+                  "chunks that stage candidates in outIdx)", maxBlocks);
+  }
   const qsa::TopkDecodeArgs a{outIdx, logits, contextLengths, splitCounters,
                               splitCounters != nullptr ? numKVHeads : 0, batchSize, maxBlocks};
   TRY(device_ready());

@@ -273,10 +273,14 @@ def test_next_rows_validation(qsa, host):
     # rows of more than 32768 blocks take one workgroup per chunk of up to 8 (8192 to 32768
     # keys each): the grid is batchSize * chunks (valid calls: no device here, no launch)
     ND = qsa.QSA_E_NO_DEVICE
-    assert tkd(B=2**20 - 1, mb=65536) == ND                   # 8 chunks: 2^23 - 8 workgroups
-    assert tkd(B=2**20, mb=65536) == E
-    assert tkd(B=2**21, mb=32772) == E                        # 5 chunks of 8192
+    far = h.p(0) + (2**20) * 65536 * 4 + 4096                 # outIdx past the largest logits
+    assert tkd(B=2**20 - 1, mb=65536, out=far) == ND          # 8 chunks: 2^23 - 8 workgroups
+    assert tkd(B=2**20, mb=65536, out=far) == E
+    assert tkd(B=2**21, mb=32772, out=far) == E               # 5 chunks of 8192
     assert tkd(B=2**21 - 1, mb=262145) == ND                  # longer rows: one per sequence
+    # split rows stage candidates in outIdx: it may not overlap logits
+    assert tkd(out=h.p(1), lg=h.p(1), mb=65536) == E
+    assert tkd(out=h.p(1), lg=h.p(1), mb=32768) == ND          # one workgroup per row: allowed
     assert tkd(mb=512, lg=None) != E                          # nVis <= 512 reads no logits
     assert tkd(B=0, out=None) == OK
 
