@@ -120,6 +120,59 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Value of lane (lane ^ j) of the wave, j in {1, 2, 4, 8, 16, 32}, by DPP and the permlane
+// swaps (VALU; no LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2;
+// row_half_mirror then quad_perm [3,2,1,0] for 4 (lane ^ 7 ^ 3); row_ror:8 for 8; for 16 and
+// 32 the swap of a register with itself leaves the wanted row (pair) in one of its two results.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int j) {
+  const int lane = threadIdx.x & 63;
+  switch (j) {
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    case 4:
+      return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B,
+                                      0xF, 0xF, false);
+    case 8: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16) ? p[0] : p[1];
+    }
+    default: {
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32) ? p[0] : p[1];
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int j) {
+  return ((uint64_t)xor_lane((uint32_t)(v >> 32), j) << 32) | xor_lane((uint32_t)v, j);
+}
+
+// Inclusive sums over the 64 lanes of a wave by DPP: within each 16-lane row by shifts of 1,
+// 2, 4 and 8 lanes (zero from outside the row), then the totals of the other rows, read from
+// their end lanes.  wave_prefix gives lane l the sum over lanes 0..l, wave_suffix over l..63.
+__device__ __forceinline__ int wave_prefix(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+__device__ __forceinline__ int wave_suffix(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x101, 0xF, 0xF, true);  // row_shl:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x102, 0xF, 0xF, true);  // row_shl:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, true);  // row_shl:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0xF, true);  // row_shl:8
+  const int r1 = __builtin_amdgcn_readlane(x, 16), r2 = __builtin_amdgcn_readlane(x, 32),
+            r3 = __builtin_amdgcn_readlane(x, 48);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row < 1 ? r1 : 0) + (row < 2 ? r2 : 0) + (row < 3 ? r3 : 0);
+}
+
 // The row's keys into registers (padding u = 0).  No load sits behind a branch, so the
 // compiler keeps several in flight (a per-group branch had it wait for each load in turn).
 // kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
@@ -163,12 +216,7 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* slot, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_prefix(v);
   if (lane == 63) slot[wave] = incl;
   __syncthreads();
   int before = 0, all = 0;
@@ -230,13 +278,8 @@ __device__ __forceinline__ void find_bin(RegShared& sh, int kRem, int p) {
     const int* hist = sh.hist[p & 1];
     const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
     const int s3 = h3, s2 = h2 + s3, s1 = h1 + s2, s0 = h0 + s1;
-    int incl = s0;  // keys in bins >= 4l
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_down(incl, o);
-      if (l + o < 64) incl += t;
-    }
-    const int ex = incl - s0;  // keys in bins >= 4l + 4
+    const int incl = wave_suffix(s0);  // keys in bins >= 4l
+    const int ex = incl - s0;          // keys in bins >= 4l + 4
     const int cum[4] = {ex + s0, ex + s1, ex + s2, ex + s3};
     const int h[4] = {h0, h1, h2, h3};
 #pragma unroll
@@ -338,12 +381,19 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     for (int r = 0; r < KPT; ++r)
       if (key_id<NT>(r, tid) < n) tmin = u[r] < tmin ? u[r] : tmin;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t a = __shfl_xor(tmax, o), b = __shfl_xor(tmin, o);
+  // wave maximum and minimum by DPP and permlane swaps (written out: xor_lane needs constant
+  // strides)
+  auto step = [&](int o) {
+    const uint32_t a = xor_lane(tmax, o), b = xor_lane(tmin, o);
     tmax = a > tmax ? a : tmax;
     tmin = b < tmin ? b : tmin;
-  }
+  };
+  step(32);
+  step(16);
+  step(8);
+  step(4);
+  step(2);
+  step(1);
   if (lane == 0) {
     sh.red[0][wave] = tmax;
     sh.red[1][wave] = tmin;
@@ -419,13 +469,7 @@ __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_
   const int2 pr = lane < (G * W) / 2 ? reinterpret_cast<const int2*>(sh.gcnt)[lane]
                                      : make_int2(0, 0);
   const int pair = pr.x + pr.y;
-  int incl = pair;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  const int exPair = incl - pair;
+  const int exPair = wave_prefix(pair) - pair;
   // T through an empty asm: the comparisons are made again per group rather than the first
   // loop's lane masks held across the barrier (two SGPR pairs per key)
   uint32_t T2 = T;
@@ -499,33 +543,6 @@ __device__ __forceinline__ void ordered_select_row(const float* row, int n, uint
   __syncthreads();
 }
 
-// Value of lane (lane ^ j) of the wave, j in {1, 2, 4, 8, 16, 32}, by DPP and the permlane
-// swaps (VALU; no LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2;
-// row_half_mirror then quad_perm [3,2,1,0] for 4 (lane ^ 7 ^ 3); row_ror:8 for 8; for 16 and
-// 32 the swap of a register with itself leaves the wanted row (pair) in one of its two results.
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int j) {
-  const int lane = threadIdx.x & 63;
-  switch (j) {
-    case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-    case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-    case 4:
-      return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B,
-                                      0xF, 0xF, false);
-    case 8: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
-    case 16: {
-      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-      return (lane & 16) ? p[0] : p[1];
-    }
-    default: {
-      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-      return (lane & 32) ? p[0] : p[1];
-    }
-  }
-}
-
-__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int j) {
-  return ((uint64_t)xor_lane((uint32_t)(v >> 32), j) << 32) | xor_lane((uint32_t)v, j);
-}
 
 // Bitonic sort, descending, of kRT * E 64-bit values; thread t holds elements e * kRT + t.
 // The stages with strides 64 and 128 go through LDS, alternating between buf0 and buf1: a
@@ -864,13 +881,7 @@ __device__ __forceinline__ void wave_window_select(Key key, int cnt, int* hist, 
     // lane l holds bins 4l .. 4l + 3; suffix sums over the lanes from bin 255 down
     const int4 h = *reinterpret_cast<const int4*>(&hist[4 * lane]);
     const int s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
-    int incl = s0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_down(incl, o);
-      if (lane + o < 64) incl += t;
-    }
-    const int ex = incl - s0;  // keys in bins >= 4l + 4
+    const int ex = wave_suffix(s0) - s0;  // keys in bins >= 4l + 4
     const int cum[4] = {ex + s0, ex + s1, ex + s2, ex + s3};
     const int hq[4] = {h.x, h.y, h.z, h.w};
     int myBin = 0, myAbove = 0, myIn = 0;
