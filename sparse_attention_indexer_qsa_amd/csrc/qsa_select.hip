@@ -503,6 +503,67 @@ __device__ __forceinline__ void ordered_select(const uint32_t (&u)[KPT], uint32_
   __syncthreads();
 }
 
+// The same selection, emitted from the LDS candidates when select_threshold kept them (every
+// key >= T is then among candU/candId[0, nc)): the selected ids are marked in two bitmaps over
+// [0, n) (keys above T, keys equal to T) and each thread ranks the ids of its own 64-id
+// stretch from the counts of the stretches below it (one block scan).  sh.selId[pos] =
+// value(id).  The bitmaps live in sh.sortBuf: clear_select_bits must have cleared them
+// before the select.  NT * 64 >= n.
+constexpr int kBitWords = 1024;  // bitmap words: ids below 32768
+// From 32 keys per thread on the bitmap emission is the faster one (rows of 16384 / 32768
+// blocks: 9.6 / 13.0 us per 64 sequences against 11.7 / 18.7; 262144-block rows split into
+// 32768-key chunks: 33.6 against 43.4); with 16 keys per thread or fewer the register form
+// is (16: 11.6 against 15.9 us on the 64-sequence decode batch).
+constexpr int kBitsMinKeys = 32;
+template <int NT>
+__device__ __forceinline__ void clear_select_bits(int n, RegShared& sh) {
+  static_assert(sizeof(sh.sortBuf) >= 2 * kBitWords * 4, "two bitmaps fit sortBuf");
+  uint32_t* bits = reinterpret_cast<uint32_t*>(sh.sortBuf);
+  const int words = 2 * ((n + 63) / 64);
+  for (int q = threadIdx.x; q < words; q += NT) {
+    bits[q] = 0u;
+    bits[kBitWords + q] = 0u;
+  }
+}
+
+template <int NT, class Value>
+__device__ __forceinline__ void ordered_select_bits(int n, int nc, uint32_t T, int need,
+                                                    RegShared& sh, Value value) {
+  static_assert(NT * 64 >= 32 * kBitWords, "a 64-id stretch per thread covers the bitmaps");
+  uint32_t* bitsA = reinterpret_cast<uint32_t*>(sh.sortBuf);
+  uint32_t* bitsT = bitsA + kBitWords;
+  const int tid = threadIdx.x;
+  for (int q = tid; q < nc; q += NT) {
+    const uint32_t uq = sh.candU[q];
+    if (uq >= T) {
+      const int id = sh.candId[q];
+      atomicOr(uq > T ? &bitsA[id >> 5] : &bitsT[id >> 5], 1u << (id & 31));
+    }
+  }
+  __syncthreads();
+  uint64_t am = 0ull, tm = 0ull;
+  if (64 * tid < n) {
+    am = (uint64_t)bitsA[2 * tid] | ((uint64_t)bitsA[2 * tid + 1] << 32);
+    tm = (uint64_t)bitsT[2 * tid] | ((uint64_t)bitsT[2 * tid + 1] << 32);
+  }
+  int total;
+  const int ex = block_excl_scan<NT>(__popcll(am) | (__popcll(tm) << 16), sh.wcnt[0], &total);
+  int aRun = ex & 0xFFFF, tRun = ex >> 16;  // keys above T / equal to T with smaller ids
+  for (uint64_t m = am | tm; m != 0ull; m &= m - 1ull) {
+    const int bit = __builtin_ctzll(m);
+    const int id = 64 * tid + bit;
+    if ((am >> bit) & 1ull) {
+      const int pos = aRun + (tRun < need ? tRun : need);
+      if (pos < kTopK) sh.selId[pos] = value(id);
+      ++aRun;
+    } else {
+      if (tRun < need) sh.selId[aRun + tRun] = value(id);
+      ++tRun;
+    }
+  }
+  __syncthreads();
+}
+
 // ordered_select over the row in memory rather than registers: the same selection in
 // ascending id, 1024 keys per step (4 consecutive ids per thread).  Used by prefill only for
 // rows with many keys equal to T, where the cached row is read again.
@@ -691,9 +752,13 @@ void topk_expand_decode_reg_kernel(TopkDecodeArgs a) {
     const float* row = a.logits + b * a.maxBlocks;
     uint32_t u[KPT];
     load_keys<kDT, KPT, kVec>(row, n, u);
+    if (KPT >= kBitsMinKeys) clear_select_bits<kDT>(n, sh);
     const Threshold th = select_threshold<kDT, KPT>(u, n, kSel, sh);
     // the selection gathers in LDS by rank and is written out in order, 4 tokens per block
-    ordered_select<kDT, KPT>(u, th.T, th.need, sh, [](int id, int) { return id; });
+    if (KPT >= kBitsMinKeys && th.nc >= 0)
+      ordered_select_bits<kDT>(n, th.nc, th.T, th.need, sh, [](int id) { return id; });
+    else
+      ordered_select<kDT, KPT>(u, th.T, th.need, sh, [](int id, int) { return id; });
     for (int s = tid; s < 4 * kSel; s += kDT) out[s] = 4 * sh.selId[s >> 2] + (s & 3);
   }
   write_tail_and_pad(out, 4 * kSel, n, (int)(c % 4), kDT);
@@ -732,8 +797,12 @@ void topk_decode_chunk_kernel(TopkDecodeArgs a) {
   const float* row = a.logits + b * a.maxBlocks + (int64_t)j * a.chunk;
   uint32_t u[KPT];
   load_keys<kDT, KPT, kVec>(row, nj, u);
+  if (KPT >= kBitsMinKeys) clear_select_bits<kDT>(nj, sh);
   const Threshold th = select_threshold<kDT, KPT>(u, nj, kTopK, sh);
-  ordered_select<kDT, KPT>(u, th.T, th.need, sh, [](int id, int) { return id; });
+  if (KPT >= kBitsMinKeys && th.nc >= 0)
+    ordered_select_bits<kDT>(nj, th.nc, th.T, th.need, sh, [](int id) { return id; });
+  else
+    ordered_select<kDT, KPT>(u, th.T, th.need, sh, [](int id, int) { return id; });
   // two ids a word: chunk j's 512 ids are bytes [1024 j, 1024 j + 1024) of the output row
   uint32_t* st = reinterpret_cast<uint32_t*>(a.outIdx + b * kIndexWidth) + j * (kTopK / 2);
   const int tid = threadIdx.x;
