@@ -32,6 +32,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "qsa_device.h"
 
 namespace qsa {
@@ -135,15 +137,12 @@ void scores_kernel(ScoresArgs a) {
   char* waveRow = reinterpret_cast<char*>(a.logits + (seqRow0 + tw0 - rowLo) * (int64_t)nB);
   const uint32_t boff = ((uint32_t)kg * (uint32_t)nB + (uint32_t)i) * 4u;
   const uint32_t rowBytes = (uint32_t)nB * 4u;
-  // chunks below fastHi are seen in full by all 16 tokens of the wave, all of them live
-  const bool waveLive = tw0 >= tLo && tw0 + kSTokWave <= tHi && tw0 + kSTokWave <= ctx;
-  const int fastHi = waveLive ? ((tw0 + 1) / 4 < rangeHi ? (tw0 + 1) / 4 : rangeHi) : 0;
 
   // staging: 64 rows x 16 pieces per chunk, rows srow + 32 p for each thread.  Rows
   // that no token of the workgroup can see, or past the range, repeat the last row the
-  // workgroup can see (fetch runs only when that row exists): the logits they feed are all
-  // masked (-FLT_MAX) or not stored.  Straight-line loads with no zero fill keep the compiler
-  // from waiting on them before they are needed.
+  // workgroup can see (fetch runs only when that row exists, i.e. when computeHi > rangeLo):
+  // the logits they feed are all masked (-FLT_MAX) or not stored.  Straight-line loads with no
+  // zero fill keep the compiler from waiting on them before they are needed.
   const uint16_t* kbSeq = static_cast<const uint16_t*>(a.kbar) + b * nB * (int64_t)kDim;
   constexpr int kRowsPerPass = kSThreads / 16;   // rows staged by one piece index (32)
   const int srow = tid >> 4, spiece = 8 * (tid & 15);
@@ -173,12 +172,24 @@ void scores_kernel(ScoresArgs a) {
   // would also wait for the next chunk's prefetch (vmcnt(0); expcnt and lgkmcnt unchanged)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   int buf = 0;
-  for (int c0 = rangeLo; c0 < fillLo; c0 += kSChunk) {
+  // One chunk of 64 blocks.  The next chunk's kbar loads are issued first, the contraction and
+  // this chunk's stores follow, and the loaded pieces go to LDS last.  Vector memory operations
+  // complete in issue order, so the wait for those loads covers only stores issued before
+  // them, those of the previous chunk, never the ones just issued.  The compiler would move
+  // the LDS writes up to the loads (ending the overlap); an empty asm statement that claims to
+  // rewrite the loaded registers, placed after the stores, keeps them there.  kFast: every
+  // token of every wave sees the whole chunk, so the stores take no masks; they go through a
+  // buffer descriptor on the chunk's first row (scalar registers) with the lane's offset in one
+  // VGPR and the row offset in a scalar register.
+  auto chunk = [&](int c0, auto fastTag) {
+    constexpr bool kFast = decltype(fastTag)::value;
     __syncthreads();  // chunk c0 is in kb_lds[buf]; every wave is done with the other buffer
-    const bool more = c0 + kSChunk < computeHi;
-    if (more) fetch(c0 + kSChunk);  // in flight during the contraction
+    fetch(c0 + kSChunk);  // past computeHi: the last row again, staged but never read
     char* chunkRow = waveRow + 4 * (int64_t)c0;
-    const bool fast = c0 + kSChunk <= fastHi;
+    // data format 32 bits (the field must be non-zero for untyped stores); no range limit:
+    // every offset used is below 16 * 4 * numBlocks <= 2^32
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(chunkRow, 0, -1, 0x00020000);
 #pragma unroll
     for (int ct = 0; ct < kSColTiles; ++ct) {
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
@@ -198,32 +209,40 @@ void scores_kernel(ScoresArgs a) {
         x[1][m] = scale * relu_head_sum(acc1[4 * m], acc1[4 * m + 1], acc1[4 * m + 2],
                                         acc1[4 * m + 3]);
       }
-      char* tileRow = chunkRow + 4 * kSColTile * ct;
-      if (fast) {
+      const int g = c0 + kSColTile * ct + i;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            __builtin_nontemporal_store(
-                x[rt][m], reinterpret_cast<float*>(tileRow + boff + (8 * rt + 2 * m) * rowBytes));
-      } else {
-        const int g = c0 + kSColTile * ct + i;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t rowOff = 4u * kSColTile * ct + (8u * rt + 2u * m) * rowBytes;
+          if constexpr (kFast) {
+            // cache policy 2: non-temporal
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x[rt][m]), rs,
+                                                  (int)boff, (int)rowOff, 2);
+          } else {
             const int tok = tw0 + 8 * rt + 2 * m + kg;
             const int nVisOut = tok < ctx ? (tok + 1) / 4 : 0;
             if (tok >= tLo && tok < tHi && g < rangeHi)
               __builtin_nontemporal_store(
                   g < nVisOut ? x[rt][m] : -FLT_MAX,
-                  reinterpret_cast<float*>(tileRow + boff + (8 * rt + 2 * m) * rowBytes));
+                  reinterpret_cast<float*>(chunkRow + boff + rowOff));
           }
-      }
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) stash(buf ^ 1);
+#pragma unroll
+    for (int p = 0; p < kSPieces; ++p)
+      asm volatile("" : "+v"(v[p].x), "+v"(v[p].y), "+v"(v[p].z), "+v"(v[p].w) :: "memory");
+    stash(buf ^ 1);
     buf ^= 1;
-  }
+  };
+  // chunks below fastAll are seen in full by all 128 tokens of the workgroup, all live; the
+  // two loops keep the unmasked one free of branches, so its waits are exact
+  const bool wgLive = t0 >= tLo && t0 + kSTokWG <= tHi && t0 + kSTokWG <= ctx;
+  const int fastAll = wgLive ? ((t0 + 1) / 4 < rangeHi ? (t0 + 1) / 4 : rangeHi) : rangeLo;
+  int c0 = rangeLo;
+  for (; c0 + kSChunk <= fastAll; c0 += kSChunk) chunk(c0, std::true_type{});
+  for (; c0 < fillLo; c0 += kSChunk) chunk(c0, std::false_type{});
   // -FLT_MAX over [fillLo, rangeHi) of each of the wave's 16 token rows, each row written in
   // contiguous 1 KB runs (64 lanes x 16 bytes)
   const bool vec = (nB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
