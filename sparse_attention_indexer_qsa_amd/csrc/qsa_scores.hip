@@ -22,10 +22,11 @@
 //    for its 16 registers v: registers 4m..4m+3 are the four heads of token 2m + lane/32 of
 //    the tile.  ReLU, the ascending head sum and the scale are in-lane; lanes 0..31 then store
 //    32 consecutive logits of one token (a 128-byte line) and lanes 32..63 those of the next.
-//  * Chunks that every token of the wave sees in full take a path without masks; the chunk
-//    holding a token's visibility edge masks per entry.  Column tiles that no token of the
-//    workgroup can see skip the contraction and store -FLT_MAX.  The kernel is bound by the
-//    FP32 logits it writes.
+//  * Chunks that every token of the workgroup sees in full run in a loop of their own with no
+//    masks (buffer stores from a scalar row base); the chunks holding visibility edges mask
+//    per entry.  Column tiles that no token of the workgroup can see skip the contraction
+//    and store -FLT_MAX.  The kernel is bound by the FP32 logits it writes: the visible
+//    pieces and the -FLT_MAX runs share the HBM write bandwidth.
 //
 // Decode gathers kbar rows from the paged pool and scores them on MFMA too (16x16x32, the
 // sequence's four heads as the A rows): the kernel is bound by those gathers.
