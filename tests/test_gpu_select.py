@@ -218,7 +218,7 @@ def test_expand_prefill(qsa, O, case):
     assert np.array_equal(ref2, ref)
 
 
-@pytest.mark.parametrize("maxBlocks", [4096, 512, 600, 2000, 1001, 32768, 40000, 0, 1, 3])
+@pytest.mark.parametrize("maxBlocks", [4096, 512, 600, 2000, 1001, 9000, 16384, 32768, 40000, 0, 1, 3])
 def test_topk_expand_decode(qsa, O, maxBlocks):
     """64 sequences: ctx <= 0, ctx/4 below, at and above 512, above 4*maxBlocks (capped), all
     four logit styles including -inf and NaNs of both signs."""
