@@ -194,12 +194,17 @@ void scores_kernel(ScoresArgs a) {
 #pragma unroll
     for (int ct = 0; ct < kSColTiles; ++ct) {
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+      // raised wave priority while the MFMAs issue: a wave in its epilogue (VALU) yields the
+      // issue slot to one still feeding the matrix core, so the two overlap across waves
+      // (241-247 -> 236-238 us on the long-prefill rows)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const uint4 bk = kb_lds[buf][kSColTile * ct + i][2 * ks + kg];
         acc0 = mfma32(T{}, qa[0][ks], bk, acc0);
         acc1 = mfma32(T{}, qa[1][ks], bk, acc1);
       }
+      __builtin_amdgcn_s_setprio(0);
       // epilogue: registers 4m..4m+3 of tile rt hold the four heads of token 8 rt + 2m + kg
       // for block i of the column tile; ReLU per head, ascending head sum, scale
       float x[2][4];
