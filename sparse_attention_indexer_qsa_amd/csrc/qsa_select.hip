@@ -85,15 +85,21 @@ __device__ __forceinline__ void write_tail_and_pad(int* out, int from, int64_t n
 // ------------------------------------------------------------------ register-resident ---
 
 struct RegShared {
-  int hist[2][256];          // radix histograms, alternating between passes
+  int hist[3][256];          // radix histograms, taking turns between passes
   int wcnt[2][kMaxW];        // per-wave counts (double-buffered by caller's parity)
   int gcnt[16 * kMaxW];      // ordered_select: per register group and wave, packed counts
   uint32_t red[2][kMaxW];    // per-wave max / min
-  int found[2][2];           // per histogram buffer: chosen bin, keys above it
-  uint32_t candU[kCandCap];
-  int32_t candId[kCandCap];
+  int ncand;                 // keys placed in candU/candId so far (compact_keys)
+  int rankBig;               // rank_sort: a bucket holds more than kRankMaxBin composites
+  // 256-byte aligned: a candidate's slot is addressed from one base with constant offsets
+  alignas(256) uint32_t candU[kCandCap];
+  alignas(256) int32_t candId[kCandCap];
   uint64_t sortBuf[2 * kTopK];
-  int32_t selId[kTopK + 64];  // ordered_select: ranks kTopK.. take the unselected keys' writes
+  union {
+    // rank_sort: per bucket, count | first slot << 16; dead once the composites are placed
+    uint32_t rankBins[1024];
+    int32_t selId[kTopK + 64];  // ordered_select: ranks kTopK.. take the unselected keys' writes
+  };
 };
 
 // Id of register key r of thread tid in a workgroup of NT threads.
@@ -244,10 +250,16 @@ __device__ __forceinline__ void launder(uint32_t (&u)[KPT]) {
 // refresh() runs between the counting and the storing loop.
 template <int NT, int ITEMS, class Pred, class Store, class Refresh>
 __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, RegShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int cnt = 0;
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) cnt += __popcll(__ballot(pred(k)));
+  for (int k = 0; k < ITEMS; ++k) {
+    cnt += __popcll(__ballot(pred(k)));
+    // keeps the scheduler from issuing every comparison first and holding all the lane masks
+    // (two scalar registers per item, spilled to vector lanes at 72 items)
+    if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+  }
   if (lane == 0) sh.wcnt[0][wave] = cnt;
   __syncthreads();
   int base = 0, total = 0;
@@ -257,6 +269,8 @@ __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, 
     base += w < wave ? c : 0;
     total += c;
   }
+  // wave-uniform: kept in a scalar register, so the running base costs no vector work per key
+  base = __builtin_amdgcn_readfirstlane(base);
   refresh();
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
@@ -269,26 +283,72 @@ __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, 
   return total;
 }
 
-// One wave finds the bin of histogram buffer p & 1 holding the kRem-th largest key (counting
-// from bin 255 down) and the number of keys in bins above it, into sh.found[p & 1]; the block
-// reads them after the caller's next barrier.
-__device__ __forceinline__ void find_bin(RegShared& sh, int kRem, int p) {
-  if (threadIdx.x < 64) {
-    const int l = threadIdx.x;
-    const int* hist = sh.hist[p & 1];
-    const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
-    const int s3 = h3, s2 = h2 + s3, s1 = h1 + s2, s0 = h0 + s1;
-    const int incl = wave_suffix(s0);  // keys in bins >= 4l
-    const int ex = incl - s0;          // keys in bins >= 4l + 4
-    const int cum[4] = {ex + s0, ex + s1, ex + s2, ex + s3};
-    const int h[4] = {h0, h1, h2, h3};
+// The register keys >= T, with their ids, into candU/candId[0, sh.ncand) in an unspecified
+// order (every later use of the candidates is independent of it); sh.ncand must be 0 before.
+// Each wave takes its keys in batches of 8 register slots: one comparison per key gives the
+// lane mask that both counts the batch and masks the key's store, and one LDS atomic per batch
+// (by lane 0, on the scalar total) reserves the batch's slots.  Ends with a barrier.
+template <int NT, int KPT>
+__device__ __forceinline__ void compact_keys(const uint32_t (&u)[KPT], uint32_t T,
+                                             RegShared& sh) {
+  constexpr int kBatch = 8;
+  static_assert(KPT % kBatch == 0 || KPT < kBatch, "whole batches of register keys");
+  constexpr int kB = KPT < kBatch ? KPT : kBatch;
+  // 4 * tid through an empty asm: each key's id is then one add of a constant
+  int ft4 = fresh_tid() << 2;
+  asm volatile("" : "+v"(ft4));
+  // a zero the compiler cannot see: the counter's address then looks lane-dependent, so the
+  // one-lane atomic is not rewritten into a wave reduction
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  const bool lane0 = (threadIdx.x & 63) == 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (cum[q] >= kRem && cum[q] - h[q] < kRem) {
-        sh.found[p & 1][0] = 4 * l + q;
-        sh.found[p & 1][1] = cum[q] - h[q];
+  for (int k0 = 0; k0 < KPT; k0 += kB) {
+    uint64_t m[kB];
+    int pre[kB], sum = 0;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      m[b] = __ballot(u[k0 + b] >= T);
+      pre[b] = sum;
+      sum += __popcll(m[b]);
+    }
+    if (sum != 0) {  // wave-uniform
+      int base = 0;
+      if (lane0) base = atomicAdd(&sh.ncand + zero, sum);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int r = k0 + b;
+        if (u[r] >= T) {  // the comparison of the ballot above
+          const int pos = base + pre[b] + lanes_below(m[b]);
+          sh.candU[pos] = u[r];
+          sh.candId[pos] = ft4 + ((r >> 2) * NT * 4 + (r & 3));  // key_id<NT>(r, tid)
+        }
       }
+    }
   }
+  __syncthreads();
+}
+
+// Every wave finds, on its own, the bin of a 256-bin histogram holding the kRem-th largest key
+// (counting from bin 255 down), the number of keys in bins above it and in it (wave-uniform
+// results; no barrier).  Lane l reads bins 4l..4l+3.  kRem <= the histogram's total.
+struct BinPick {
+  int bin, above, inBin;
+};
+__device__ __forceinline__ BinPick find_bin(const int* hist, int kRem) {
+  const int l = threadIdx.x & 63;
+  const int4 h = reinterpret_cast<const int4*>(hist)[l];
+  const int s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
+  const int incl = wave_suffix(s0);  // keys in bins >= 4l
+  const int ex = incl - s0;          // keys in bins >= 4l + 4
+  const int src = __builtin_ctzll(__ballot(ex < kRem && kRem <= incl));
+  // within the lane: the highest bin 4l+q whose keys in bins >= 4l+q reach kRem
+  const int q = ex + s3 >= kRem ? 3 : ex + s2 >= kRem ? 2 : ex + s1 >= kRem ? 1 : 0;
+  const int above = q == 3 ? ex : q == 2 ? ex + s3 : q == 1 ? ex + s2 : ex + s1;
+  const int inBin = q == 3 ? h.w : q == 2 ? h.z : q == 1 ? h.y : h.x;
+  return BinPick{4 * src + __builtin_amdgcn_readlane(q, src),
+                 __builtin_amdgcn_readlane(above, src), __builtin_amdgcn_readlane(inBin, src)};
 }
 
 // Radix window [wlo, wlo + wm1] holding the kRem-th largest of the keys it covers.
@@ -301,10 +361,9 @@ struct RadixWindow {
 
 // One radix pass: histogram of the window's keys (registers, or the nc LDS candidates) over
 // 256 bins at a shift that spreads the window over them, then narrow the window to the bin
-// holding the kRem-th largest.
-// Pass p histograms into buffer p & 1, which the previous pass (or the caller, for p = 0)
-// cleared; it clears the other buffer for the next pass once every thread is past the barrier
-// that follows the histogram, so no thread still reads it.
+// holding the kRem-th largest.  Pass p histograms into buffer p % 3, which was cleared before
+// the barrier that precedes the pass, and clears buffer (p + 1) % 3 for the next pass: every
+// wave last read that buffer in pass p - 2, before the barrier of pass p - 1.  One barrier.
 template <int NT, int KPT, bool kLds>
 __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, RadixWindow& w,
                                            RegShared& sh, int p) {
@@ -312,7 +371,7 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, Rad
   const int bits = w.wm1 ? 32 - __clz(w.wm1) : 0;
   const int shift = bits > 8 ? bits - 8 : 0;
   const uint32_t wlo = w.wlo, wm1 = w.wm1;
-  int* hist = sh.hist[p & 1];
+  int* hist = sh.hist[p % 3];
   if constexpr (kLds) {
     for (int c = tid; c < nc; c += NT) {
       const uint32_t d = sh.candU[c] - wlo;
@@ -327,19 +386,13 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, Rad
       if (d <= wm1) atomicAdd(&hist[d >> shift], one);
     }
   }
-  __syncthreads();  // the histogram is complete; every thread is done with the previous pass
-  find_bin(sh, w.kRem, p);
-  int* next = sh.hist[(p + 1) & 1];
+  int* next = sh.hist[(p + 1) % 3];
   for (int j = tid; j < 256; j += NT) next[j] = 0;
-  if (tid == 0) {
-    sh.found[(p + 1) & 1][0] = 0;
-    sh.found[(p + 1) & 1][1] = 0;
-  }
-  __syncthreads();
-  const int bin = sh.found[p & 1][0] & 255, above = sh.found[p & 1][1];
-  w.inBin = hist[bin];
-  w.kRem -= above;
-  const uint32_t off = (uint32_t)bin << shift;
+  __syncthreads();  // the histogram is complete
+  const BinPick pick = find_bin(hist, w.kRem);
+  w.inBin = pick.inBin;
+  w.kRem -= pick.above;
+  const uint32_t off = (uint32_t)pick.bin << shift;
   w.wlo = wlo + off;
   const uint32_t binM1 = (1u << shift) - 1u, restM1 = wm1 - off;
   w.wm1 = binM1 < restM1 ? binM1 : restM1;
@@ -351,6 +404,7 @@ struct Threshold {
   int need;     // keys equal to T that are selected (the smallest ids among them)
   int ties;     // keys equal to T
   int nc;       // keys in LDS candidates (candU/candId), -1 when the passes ran on registers
+  uint32_t hi;  // the row's largest key
 };
 
 // Exact radix select of the kSel-th largest key of the (padded) row held in registers, kSel <= n.
@@ -399,10 +453,7 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
     sh.red[1][wave] = tmin;
   }
   for (int j = tid; j < 256; j += NT) sh.hist[0][j] = 0;  // the first pass's histogram
-  if (tid == 0) {
-    sh.found[0][0] = 0;
-    sh.found[0][1] = 0;
-  }
+  if (tid == 0) sh.ncand = 0;
   __syncthreads();
   uint32_t hi = 0u, lo = 0xFFFFFFFFu;
 #pragma unroll
@@ -412,28 +463,22 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   }
   RadixWindow w{lo, hi - lo, kSel, 0, 0};
   radix_pass<NT, KPT, false>(u, 0, w, sh, 0);
-  if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, -1};
+  if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, -1, hi};
   // keep the keys >= wlo in LDS (those above the new window are selected for certain).  Kept
   // out of the pass loop below, so that no per-key value of it is hoisted into registers that
   // stay live across the passes.
   int nc = -1;
   if ((kSel - w.kRem) + w.inBin <= kCandCap) {
-    const uint32_t T = w.wlo;
-    const int ft = fresh_tid();
-    nc = compact<NT, KPT>(
-        [&](int r) { return u[r] >= T; },
-        [&](int pos, int r) {  // pos < kCandCap: exactly (kSel - kRem) + inBin keys are >= T
-          sh.candU[pos] = u[r];
-          sh.candId[pos] = key_id<NT>(r, ft);
-        },
-        [&] { launder<KPT>(u); }, sh);
+    // exactly (kSel - kRem) + inBin <= kCandCap keys are >= wlo
+    compact_keys<NT, KPT>(u, w.wlo, sh);
+    nc = sh.ncand;
   }
   for (int pass = 1; pass < 5; ++pass) {
     if (nc >= 0) radix_pass<NT, KPT, true>(u, nc, w, sh, pass);
     else radix_pass<NT, KPT, false>(u, 0, w, sh, pass);
-    if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, nc};
+    if (w.shift == 0) return Threshold{w.wlo, w.kRem, w.inBin, nc, hi};
   }
-  return Threshold{w.wlo, w.kRem, 0, nc};  // not reached: the shift reaches 0 within 4 passes
+  return Threshold{w.wlo, w.kRem, 0, nc, hi};  // not reached: the shift reaches 0 within 4 passes
 }
 
 // The selected keys in ascending id (registers): above T, then the first `need` keys equal to
@@ -666,6 +711,80 @@ __device__ __forceinline__ void sort_selected(int m, int kSel, RegShared& sh) {
   __syncthreads();
 }
 
+// Ordering of the m selected composites (keys in [T, hi]) by bucket ranks, where the buckets
+// are small: the key range [T, hi] is cut into kRankBins buckets by its top bits (a bucket's
+// composites all exceed those of every lower bucket), the buckets are counted and laid out in
+// descending order by one block scan, each composite is placed in its bucket, and its rank
+// inside the bucket is the number of the bucket's composites greater than it.  The composites
+// are distinct (ids differ), so the ranks are too, and the result is the order of the
+// descending sort.  A bucket of more than kRankMaxBin composites (many keys in a narrow range,
+// e.g. ties) makes the whole row take the bitonic sort of the placed composites instead; the
+// decision is the same for every thread of the row.
+// load(k, &v) gives thread tid its k-th item (k < KC) and whether it is one of the m; placed
+// (2 * kTopK entries) receives the composites in bucket order and must not alias the items'
+// source; the bitonic fallback then sorts placed[0, m) with sortBuf / candU as its buffers,
+// so placed is sortBuf, or the items are in sortBuf already and placed is any other buffer.
+// sh.rankBins and sh.rankBig must be zero before the barrier that precedes the call
+// (clear_rank_bins).  Leaves the ids of the first kSel in sh.selId; ends with a barrier.
+constexpr int kRankBins = 1024;
+constexpr int kRankMaxBin = 32;
+__device__ __forceinline__ void clear_rank_bins(RegShared& sh) {
+  static_assert(kRankBins == 4 * kRT, "four buckets per thread");
+  reinterpret_cast<uint4*>(sh.rankBins)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) sh.rankBig = 0;
+}
+
+template <int KC, class Load>
+__device__ __forceinline__ void rank_sort(int m, int kSel, uint32_t T, uint32_t hi,
+                                          uint64_t* placed, RegShared& sh, Load load) {
+  const int tid = threadIdx.x;
+  uint32_t* bins = sh.rankBins;  // per bucket in descending key order: count | start << 16
+  const uint32_t range = hi - T;
+  const int rbits = range ? 32 - __clz(range) : 0;
+  const int shift = rbits > 10 ? rbits - 10 : 0;  // (hi - T) >> shift < kRankBins
+  uint64_t v[KC];
+  int bin[KC], slot[KC];
+  bool ok[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    ok[k] = load(k, v[k]);
+    bin[k] = (kRankBins - 1) - (int)(((uint32_t)(v[k] >> 32) - T) >> shift);
+    slot[k] = ok[k] ? (int)atomicAdd(&bins[bin[k] & (kRankBins - 1)], 1u) : 0;
+  }
+  __syncthreads();
+  const uint4 c4 = reinterpret_cast<const uint4*>(bins)[tid];
+  const uint32_t s1 = c4.x, s2 = s1 + c4.y, s3 = s2 + c4.z, own = s3 + c4.w;
+  if (max(max(c4.x, c4.y), max(c4.z, c4.w)) > (uint32_t)kRankMaxBin) sh.rankBig = 1;
+  int total;
+  const uint32_t ex = (uint32_t)block_excl_scan<kRT>((int)own, sh.wcnt[0], &total);
+  reinterpret_cast<uint4*>(bins)[tid] =
+      make_uint4(c4.x | ex << 16, c4.y | (ex + s1) << 16, c4.z | (ex + s2) << 16,
+                 c4.w | (ex + s3) << 16);
+  __syncthreads();
+  uint32_t bc[KC];  // read before the barrier below: selId overlays the buckets after it
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    bc[k] = ok[k] ? bins[bin[k]] : 0u;
+    if (ok[k]) placed[(bc[k] >> 16) + slot[k]] = v[k];
+  }
+  __syncthreads();
+  if (sh.rankBig) {  // uniform: a bucket too large for the in-bucket ranks
+    if (m <= kTopK) sort_selected<kTopK / kRT>(m, kSel, sh);
+    else sort_selected<2 * kTopK / kRT>(m, kSel, sh);
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    if (ok[k]) {
+      const int b0 = (int)(bc[k] >> 16), c = (int)(bc[k] & 0xFFFFu);
+      int r = 0;
+      for (int j = 0; j < c; ++j) r += placed[b0 + j] > v[k] ? 1 : 0;
+      if (b0 + r < kSel) sh.selId[b0 + r] = (int32_t)~(uint32_t)v[k];
+    }
+  }
+  __syncthreads();
+}
+
 // Waves per SIMD the register allocation aims for at KPT keys per thread (512 VGPRs per SIMD
 // lane shared by the waves): at most 80 keys leave room for 4 rows of 4 waves on a CU.
 constexpr int reg_waves(int kpt) { return kpt <= 24 ? 5 : kpt <= 80 ? 4 : kpt <= 96 ? 3 : 2; }
@@ -688,7 +807,6 @@ void topk_expand_reg_kernel(TopkArgs a) {
   const float* row = a.logits + i * a.numBlocks;
   uint32_t u[KPT];
   if (n > 0) load_keys<kRT, KPT, kVec>(row, n, u);
-  int m;
   if (n <= kTopK) {
     // every key is taken; ids < n <= 512 all sit in register group 0
 #pragma unroll
@@ -696,35 +814,35 @@ void topk_expand_reg_kernel(TopkArgs a) {
       const int id = key_id<kRT>(q, tid);
       if (id < n) sh.sortBuf[id] = composite(u[q], id);
     }
-    m = n;
+    __syncthreads();
+    sort_selected<kTopK / kRT>(n, kSel, sh);
   } else {
+    clear_rank_bins(sh);  // ordered before rank_sort by the select's barriers
     const Threshold th = select_threshold<kRT, KPT>(u, n, kSel, sh);
-    m = (kSel - th.need) + th.ties;
+    const uint32_t T = th.T;
+    const int m = (kSel - th.need) + th.ties;
     if (th.nc >= 0 && m <= 2 * kTopK) {
-      // the keys >= T are all among the LDS candidates
-      const uint32_t T = th.T;
+      // the keys >= T are all among the LDS candidates: rank them from there
       const int nc = th.nc;
-      compact<kRT, kCandCap / kRT>(
-          [&](int k) {
-            const int q = k * kRT + tid;
-            return q < nc && sh.candU[q] >= T;
-          },
-          [&](int pos, int k) {
-            const int q = k * kRT + tid;
-            if (pos < 2 * kTopK) sh.sortBuf[pos] = composite(sh.candU[q], sh.candId[q]);
-          },
-          [] {}, sh);
+      rank_sort<kCandCap / kRT>(m, kSel, T, th.hi, sh.sortBuf, sh, [&](int k, uint64_t& v) {
+        const int q = k * kRT + tid;
+        const uint32_t uq = q < nc ? sh.candU[q] : 0u;
+        v = composite(uq, q < nc ? sh.candId[q] : 0);
+        return q < nc && uq >= T;
+      });
     } else {
       // many keys equal to T: the exact selection in ascending id, from the row in memory
-      ordered_select_row(row, n, th.T, th.need, sh, [&](int pos, int id, uint32_t uu) {
+      ordered_select_row(row, n, T, th.need, sh, [&](int pos, int id, uint32_t uu) {
         if (pos < kTopK) sh.sortBuf[pos] = composite(uu, id);
       });
-      m = kSel;
+      rank_sort<kTopK / kRT>(kSel, kSel, T, th.hi, reinterpret_cast<uint64_t*>(sh.candId), sh,
+                             [&](int k, uint64_t& v) {
+                               const int q = k * kRT + tid;
+                               v = q < kSel ? sh.sortBuf[q] : 0ull;
+                               return q < kSel;
+                             });
     }
   }
-  __syncthreads();
-  if (m <= kTopK) sort_selected<kTopK / kRT>(m, kSel, sh);
-  else sort_selected<2 * kTopK / kRT>(m, kSel, sh);
   for (int s = tid; s < 4 * kSel; s += kRT) out[s] = sh.selId[s >> 2] * 4 + (s & 3);
   write_tail_and_pad(out, 4 * kSel, nVisT, (int)((t + 1) % 4), kRT);
 }
