@@ -400,15 +400,18 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&u)[KPT], int nc, Rad
 }
 
 struct Threshold {
-  uint32_t T;   // the kSel-th largest key
-  int need;     // keys equal to T that are selected (the smallest ids among them)
+  uint32_t T;   // the kSel-th largest key (kCands: a lower bound, see select_threshold)
+  int need;     // keys equal to T that are selected (the smallest ids among them); -1: kCands
   int ties;     // keys equal to T
   int nc;       // keys in LDS candidates (candU/candId), -1 when the passes ran on registers
   uint32_t hi;  // the row's largest key
 };
 
 // Exact radix select of the kSel-th largest key of the (padded) row held in registers, kSel <= n.
-template <int NT, int KPT>
+// kCands: when the keys at or above the first pass's bin, kSel to 2 kTopK of them, are what the
+// compaction placed in LDS, stop there: T is then that bin's lower bound, every key >= T is
+// among candU/candId[0, nc) and the kSel largest of them are the selection (need = -1).
+template <int NT, int KPT, bool kCands = false>
 __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n, int kSel,
                                                      RegShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -468,10 +471,11 @@ __device__ __forceinline__ Threshold select_threshold(uint32_t (&u)[KPT], int n,
   // out of the pass loop below, so that no per-key value of it is hoisted into registers that
   // stay live across the passes.
   int nc = -1;
-  if ((kSel - w.kRem) + w.inBin <= kCandCap) {
-    // exactly (kSel - kRem) + inBin <= kCandCap keys are >= wlo
+  const int nCand = (kSel - w.kRem) + w.inBin;  // the keys >= wlo
+  if (nCand <= kCandCap) {
     compact_keys<NT, KPT>(u, w.wlo, sh);
-    nc = sh.ncand;
+    nc = nCand;
+    if (kCands && nc <= 2 * kTopK) return Threshold{w.wlo, -1, 0, nc, hi};
   }
   for (int pass = 1; pass < 5; ++pass) {
     if (nc >= 0) radix_pass<NT, KPT, true>(u, nc, w, sh, pass);
@@ -752,14 +756,25 @@ __device__ __forceinline__ void rank_sort(int m, int kSel, uint32_t T, uint32_t 
     slot[k] = ok[k] ? (int)atomicAdd(&bins[bin[k] & (kRankBins - 1)], 1u) : 0;
   }
   __syncthreads();
-  const uint4 c4 = reinterpret_cast<const uint4*>(bins)[tid];
-  const uint32_t s1 = c4.x, s2 = s1 + c4.y, s3 = s2 + c4.z, own = s3 + c4.w;
-  if (max(max(c4.x, c4.y), max(c4.z, c4.w)) > (uint32_t)kRankMaxBin) sh.rankBig = 1;
-  int total;
-  const uint32_t ex = (uint32_t)block_excl_scan<kRT>((int)own, sh.wcnt[0], &total);
-  reinterpret_cast<uint4*>(bins)[tid] =
-      make_uint4(c4.x | ex << 16, c4.y | (ex + s1) << 16, c4.z | (ex + s2) << 16,
-                 c4.w | (ex + s3) << 16);
+  {
+    // every wave scans all the buckets (lane l: buckets 16l..16l+15), so no barrier is needed
+    // between the scan and the starts; wave w writes the starts of buckets 16l+4w..16l+4w+3
+    static_assert(kRT == 256 && kRankBins == 1024, "4 waves, 16 buckets per lane");
+    const int l = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint4* b4 = reinterpret_cast<const uint4*>(bins) + 4 * l;
+    const uint4 g0 = b4[0], g1 = b4[1], g2 = b4[2], g3 = b4[3];
+    const uint32_t t0 = g0.x + g0.y + g0.z + g0.w, t1 = g1.x + g1.y + g1.z + g1.w,
+                   t2 = g2.x + g2.y + g2.z + g2.w, t3 = g3.x + g3.y + g3.z + g3.w;
+    const uint32_t seg = t0 + t1 + t2 + t3;
+    uint32_t ex = (uint32_t)wave_prefix((int)seg) - seg;  // buckets before 16l
+    const uint4 c4 = w == 0 ? g0 : w == 1 ? g1 : w == 2 ? g2 : g3;
+    ex += (w > 0 ? t0 : 0u) + (w > 1 ? t1 : 0u) + (w > 2 ? t2 : 0u);
+    if (max(max(c4.x, c4.y), max(c4.z, c4.w)) > (uint32_t)kRankMaxBin) sh.rankBig = 1;
+    const uint32_t s1 = c4.x, s2 = s1 + c4.y, s3 = s2 + c4.z;
+    reinterpret_cast<uint4*>(bins)[4 * l + w] =
+        make_uint4(c4.x | ex << 16, c4.y | (ex + s1) << 16, c4.z | (ex + s2) << 16,
+                   c4.w | (ex + s3) << 16);
+  }
   __syncthreads();
   uint32_t bc[KC];  // read before the barrier below: selId overlays the buckets after it
 #pragma unroll
@@ -818,10 +833,18 @@ void topk_expand_reg_kernel(TopkArgs a) {
     sort_selected<kTopK / kRT>(n, kSel, sh);
   } else {
     clear_rank_bins(sh);  // ordered before rank_sort by the select's barriers
-    const Threshold th = select_threshold<kRT, KPT>(u, n, kSel, sh);
+    const Threshold th = select_threshold<kRT, KPT, true>(u, n, kSel, sh);
     const uint32_t T = th.T;
     const int m = (kSel - th.need) + th.ties;
-    if (th.nc >= 0 && m <= 2 * kTopK) {
+    if (th.need < 0) {
+      // the candidates are every key >= T, kSel to 2 kTopK of them: rank them all
+      const int nc = th.nc;
+      rank_sort<kCandCap / kRT>(nc, kSel, T, th.hi, sh.sortBuf, sh, [&](int k, uint64_t& v) {
+        const int q = k * kRT + tid;
+        v = composite(q < nc ? sh.candU[q] : 0u, q < nc ? sh.candId[q] : 0);
+        return q < nc;
+      });
+    } else if (th.nc >= 0 && m <= 2 * kTopK) {
       // the keys >= T are all among the LDS candidates: rank them from there
       const int nc = th.nc;
       rank_sort<kCandCap / kRT>(m, kSel, T, th.hi, sh.sortBuf, sh, [&](int k, uint64_t& v) {
