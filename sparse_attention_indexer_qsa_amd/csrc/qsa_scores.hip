@@ -23,7 +23,9 @@
 //    the tile.  ReLU, the ascending head sum and the scale are in-lane; lanes 0..31 then store
 //    32 consecutive logits of one token (a 128-byte line) and lanes 32..63 those of the next.
 //  * Chunks that every token of the workgroup sees in full run in a loop of their own with no
-//    masks (buffer stores from a scalar row base); the chunks holding visibility edges mask
+//    masks (buffer stores from a scalar row base), walked from a chunk that depends on the
+//    tile (then around), so that the workgroups in flight write different column offsets of
+//    their rows rather than all the same one; the chunks holding visibility edges mask
 //    per entry.  Column tiles that no token of the workgroup can see skip the contraction
 //    and store -FLT_MAX.  The kernel is bound by the FP32 logits it writes: the visible
 //    pieces and the -FLT_MAX runs share the HBM write bandwidth.
@@ -161,8 +163,16 @@ void scores_kernel(ScoresArgs a) {
     for (int p = 0; p < kSPieces; ++p) kb_lds[buf][srow + kRowsPerPass * p][tid & 15] = v[p];
   };
 
+  // chunks below fastAll are seen in full by all 128 tokens of the workgroup, all live; the
+  // two loops keep the unmasked one free of branches, so its waits are exact.  The unmasked
+  // chunks are walked from a start that differs between tiles (then around), so that the
+  // workgroups in flight write different column offsets of their rows at a time
+  const bool wgLive = t0 >= tLo && t0 + kSTokWG <= tHi && t0 + kSTokWG <= ctx;
+  const int fastAll = wgLive ? ((t0 + 1) / 4 < rangeHi ? (t0 + 1) / 4 : rangeHi) : rangeLo;
+  const int nFast = fastAll > rangeLo ? (fastAll - rangeLo) / kSChunk : 0;
+  const int rot = nFast > 0 ? (int)(tile % nFast) : 0;
   if (rangeLo < computeHi) {
-    fetch(rangeLo);
+    fetch(rangeLo + kSChunk * rot);
     stash(0);
   }
   // chunks at or past fillLo hold nothing any row of the workgroup can see: they are written
@@ -182,10 +192,10 @@ void scores_kernel(ScoresArgs a) {
   // token of every wave sees the whole chunk, so the stores take no masks; they go through a
   // buffer descriptor on the chunk's first row (scalar registers) with the lane's offset in one
   // VGPR and the row offset in a scalar register.
-  auto chunk = [&](int c0, auto fastTag) {
+  auto chunk = [&](int c0, int cNext, auto fastTag) {
     constexpr bool kFast = decltype(fastTag)::value;
     __syncthreads();  // chunk c0 is in kb_lds[buf]; every wave is done with the other buffer
-    fetch(c0 + kSChunk);  // past computeHi: the last row again, staged but never read
+    fetch(cNext);  // past computeHi: the last row again, staged but never read
     char* chunkRow = waveRow + 4 * (int64_t)c0;
     // data format 32 bits (the field must be non-zero for untyped stores); no range limit:
     // every offset used is below 16 * 4 * numBlocks <= 2^32
@@ -242,13 +252,16 @@ void scores_kernel(ScoresArgs a) {
     stash(buf ^ 1);
     buf ^= 1;
   };
-  // chunks below fastAll are seen in full by all 128 tokens of the workgroup, all live; the
-  // two loops keep the unmasked one free of branches, so its waits are exact
-  const bool wgLive = t0 >= tLo && t0 + kSTokWG <= tHi && t0 + kSTokWG <= ctx;
-  const int fastAll = wgLive ? ((t0 + 1) / 4 < rangeHi ? (t0 + 1) / 4 : rangeHi) : rangeLo;
-  int c0 = rangeLo;
-  for (; c0 + kSChunk <= fastAll; c0 += kSChunk) chunk(c0, std::true_type{});
-  for (; c0 < fillLo; c0 += kSChunk) chunk(c0, std::false_type{});
+  int j = rot;
+  for (int k = 0; k < nFast; ++k) {
+    const int jn = j + 1 == nFast ? 0 : j + 1;
+    // the last unmasked chunk prefetches the first masked one
+    chunk(rangeLo + kSChunk * j, rangeLo + kSChunk * (k + 1 < nFast ? jn : nFast),
+          std::true_type{});
+    j = jn;
+  }
+  for (int c0 = rangeLo + kSChunk * nFast; c0 < fillLo; c0 += kSChunk)
+    chunk(c0, c0 + kSChunk, std::false_type{});
   // -FLT_MAX over [fillLo, rangeHi) of each of the wave's 16 token rows, each row written in
   // contiguous 1 KB runs (64 lanes x 16 bytes)
   const bool vec = (nB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
