@@ -338,14 +338,31 @@ def config_leg(qsa, torch, name, reps, warmup):
     return out
 
 
+# Each leg's warm-up lasts at least this long as well as `warmup` calls: the first tens of
+# milliseconds of a leg on a freshly allocated output run measurably slower (the scores call
+# 245 against 210 us over its first 55 calls, the selection 134 against 126), and the legs
+# report steady-state calls.
+WARM_S = 0.1
+
+
+def _warm(torch, call, warmup):
+    """Run call() `warmup` times and then until WARM_S seconds have passed, synchronised."""
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < WARM_S:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+
+
 def _time_stream(torch, fn, steps, warmup):
     """Average microseconds per call of fn() on a fresh stream, timed with stream events."""
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()  # inputs made on the default stream are complete
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            fn(stream.cuda_stream)
-        torch.cuda.synchronize()
+        _warm(torch, lambda: fn(stream.cuda_stream), warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
@@ -501,9 +518,8 @@ def scores_leg(qsa, torch, s, wl, steps, warmup, rowStart=SCORE_ROWS[0], numRows
     args = (logits.data_ptr(), s["q"].data_ptr(), s["kb"].data_ptr(), s["ctx"].data_ptr(), 1, S,
             nb, rowStart, numRows, qsa.QSA_BF16, stream.cuda_stream)
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            assert qsa.lib.qsa_index_scores(*args) == 0, qsa.qsa_last_error()
-        torch.cuda.synchronize()
+        assert qsa.lib.qsa_index_scores(*args) == 0, qsa.qsa_last_error()
+        _warm(torch, lambda: qsa.lib.qsa_index_scores(*args), warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
