@@ -176,6 +176,34 @@ def test_topk_expand_long_prefill_bench_rows(qsa, O):
     _run_long(qsa, O, 1, S, nb, ctx, r0, n, logits, "bench rows")
 
 
+def test_topk_expand_rank_paths(qsa, O):
+    """Rows of about 17500 blocks (72 register keys per thread) built so that the ranking of
+    the selected keys takes each of its paths: 600 keys tied at the maximum (every selected
+    key in one bucket: the bitonic fallback on the candidates); 700 distinct keys one ulp apart
+    at the top (buckets one ulp wide); 1200 keys tied at the threshold under 300 distinct ones
+    (too many candidates: the exact threshold, the ordered pass over the row, one large bucket);
+    900 tied under 100 distinct (1000 candidates, one large bucket); and 1100 distinct keys
+    one ulp apart (more than 1024 candidates: the exact threshold from the LDS passes, then the
+    ranks of the keys at or above it)."""
+    B, S, nb = 1, 70000, 17500
+    ctx = np.array([S], np.int32)
+    r0, n = S - 5, 5
+    rng = np.random.default_rng(31)
+    logits = rng.standard_normal((n, nb)).astype(np.float32)
+    five = np.array([5.0], np.float32).view(np.uint32)[0]
+
+    def above(k, start=0):  # k distinct keys, one ulp apart, from 5.0 + start ulps up
+        return (five + np.uint32(start) + np.arange(k, dtype=np.uint32)).view(np.float32)
+
+    for row, (tied, distinct) in enumerate([(600, 0), (0, 700), (1200, 300), (900, 100),
+                                            (0, 1100)]):
+        pos = rng.choice(nb, tied + distinct, replace=False)
+        logits[row, pos[:tied]] = np.float32(5.0)
+        if distinct:
+            logits[row, pos[tied:]] = above(distinct, 1 if tied else 0)
+    _run_long(qsa, O, B, S, nb, ctx, r0, n, logits, "rank paths")
+
+
 def test_topk_expand_all_ones_nan(qsa, O):
     """Keys at the bottom of the order (FP32 bits 0xFFFFFFFF map to 0): a row made only of
     them (the threshold is 0 and padding keys equal it), a row where one thread's keys are all
