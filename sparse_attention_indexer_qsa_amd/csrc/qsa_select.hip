@@ -1235,6 +1235,71 @@ __device__ __forceinline__ void sort_wave_desc(uint64_t (&v)[E]) {
   }
 }
 
+// The bucket ranks of rank_sort for one wave's 64 * E composites v (lane l holds entries
+// e * 64 + l; the first m are real, all with keys in [T, hi]), with the wave's own LDS: the
+// composites' source must be read already; `bins` (1024 words) and `placed` (64 * E entries)
+// are this wave's.  Every lane gets pos[e], the descending-sort position of its entry e, or
+// returns false (nothing written to pos) when a bucket holds more than kRankMaxBin of them:
+// then the caller sorts v itself.  No workgroup barrier: a wave's LDS accesses take effect in
+// issue order (wave_sync keeps the compiler from reordering them).
+template <int E>
+__device__ __forceinline__ bool rank_wave(const uint64_t (&v)[E], int m, uint32_t T, uint32_t hi,
+                                          uint32_t* bins, uint64_t* placed, int (&pos)[E]) {
+  static_assert(kRankBins == 1024, "16 buckets per lane");
+  const int lane = threadIdx.x & 63;
+  uint4* b4 = reinterpret_cast<uint4*>(bins) + 4 * lane;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) b4[q] = make_uint4(0u, 0u, 0u, 0u);
+  wave_sync();
+  const uint32_t range = hi - T;
+  const int rbits = range ? 32 - __clz(range) : 0;
+  const int shift = rbits > 10 ? rbits - 10 : 0;
+  int bin[E], slot[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool ok = 64 * e + lane < m;
+    bin[e] = ((kRankBins - 1) - (int)(((uint32_t)(v[e] >> 32) - T) >> shift)) & (kRankBins - 1);
+    slot[e] = ok ? (int)atomicAdd(&bins[bin[e]], 1u) : 0;
+  }
+  wave_sync();
+  uint4 g[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) g[q] = b4[q];
+  uint32_t big = 0u, seg = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    big = max(big, max(max(g[q].x, g[q].y), max(g[q].z, g[q].w)));
+    seg += g[q].x + g[q].y + g[q].z + g[q].w;
+  }
+  if (__ballot(big > (uint32_t)kRankMaxBin) != 0ull) return false;
+  uint32_t run = (uint32_t)wave_prefix((int)seg) - seg;  // buckets before 16 lane
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 w = g[q];
+    w.x |= run << 16; run += g[q].x;
+    w.y |= run << 16; run += g[q].y;
+    w.z |= run << 16; run += g[q].z;
+    w.w |= run << 16; run += g[q].w;
+    b4[q] = w;
+  }
+  wave_sync();
+  uint32_t bc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bc[e] = bins[bin[e]];
+    if (64 * e + lane < m) placed[(bc[e] >> 16) + slot[e]] = v[e];
+  }
+  wave_sync();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int b0 = (int)(bc[e] >> 16), c = 64 * e + lane < m ? (int)(bc[e] & 0xFFFFu) : 0;
+    int r = 0;
+    for (int j = 0; j < c; ++j) r += placed[b0 + j] > v[e] ? 1 : 0;
+    pos[e] = b0 + r;
+  }
+  return true;
+}
+
 // KPL keys per lane of the step starting at id s: lane l takes the 16-byte groups
 // s + 4 (g * 64 + l).  kVec: one 16-byte load per group (groups past n load the row's first
 // keys); otherwise one load per key at min(id, n - 1).  Raw FP32 bits; the caller masks.
@@ -1358,19 +1423,36 @@ __global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkAr
     }
     wave_sync();
   }
-  // sort the cnt = kSel selected keys; padding composites are 0 and sort last
+  // order the cnt = kSel selected keys: bucket ranks over [T, hi] (their smallest and largest
+  // keys), or the bitonic sort when a bucket is crowded; padding composites are 0
   constexpr int E = kTopK / 64;
+  static_assert(sizeof(sh.u) >= 8 * kTopK && sizeof(sh.id) >= 4 * kRankBins,
+                "the placed composites and the buckets fit the candidate buffer");
   uint64_t v[E];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = 64 * e + lane;
     v[e] = j < cnt ? composite(sh.u[j], (int)sh.id[j]) : 0ull;
+    if (j < cnt) {
+      const uint32_t uk = (uint32_t)(v[e] >> 32);
+      lo = uk < lo ? uk : lo;
+      hi = uk > hi ? uk : hi;
+    }
   }
-  sort_wave_desc<E>(v);
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  wave_sync();  // the buffer is read: it now holds the buckets and the placed composites
+  int pos[E];
+  if (!rank_wave<E>(v, cnt, lo, hi, sh.id, reinterpret_cast<uint64_t*>(sh.u), pos)) {
+    sort_wave_desc<E>(v);
+#pragma unroll
+    for (int e = 0; e < E; ++e) pos[e] = 64 * e + lane;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int p = 64 * e + lane;
-    if (p < kSel) {
+    const int p = pos[e];
+    if (64 * e + lane < cnt && p < kSel) {
       const int id = (int)~(uint32_t)v[e];
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[4 * p + j] = 4 * id + j;
