@@ -1324,12 +1324,146 @@ __device__ __forceinline__ void load_step(const float* row, int n, int s, uint32
   }
 }
 
+// One wave walks keys [0, n) of `row` and leaves the min(n, kTopK) largest of those above
+// thr0, by (u desc, id asc), in sh.u / sh.id[0, cnt); returns cnt (fewer than min(n, kTopK)
+// only when fewer keys are above thr0).  thr0 = 0: the buffer first takes the first
+// min(n, kCap) keys as they are (so a later key with u = 0 can never be among the kTopK
+// largest); thr0 > 0: only keys above thr0 ever enter.  Then a step of keys at a time, with
+// the next step's loads in flight: keys above the running threshold thr enter the buffer, and
+// a step that would not fit cuts the buffer first (wave_keep_top) and raises thr.  The step
+// past the end makes the exact cut to kTopK.
 template <int kCap, int KPL, bool kVec>
-__global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkArgs a) {
+__device__ __forceinline__ int walk_row(const float* row, int n, uint32_t thr0,
+                                        WaveShared<kCap>& sh) {
   constexpr int kStep = 64 * KPL;
   constexpr int kSlack = kCap - kStep - kTopK;  // a cut during the walk leaves room for a step
   static_assert(kCap % 256 == 0 && kSlack >= 0, "a step must fit a cut buffer");
   static_assert(KPL % 4 == 0, "keys are loaded in 16-byte groups of 4 per lane");
+  const int lane = threadIdx.x & 63;
+  int cnt = 0, first = 0;
+  if (thr0 == 0u) {
+    // the first min(n, kCap) keys, each at its id
+    constexpr int FL = kCap / 64;
+    uint32_t raw[FL];
+    load_step<FL, kVec>(row, n, 0, raw);
+#pragma unroll
+    for (int g = 0; g < FL / 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = (g * 64 + lane) * 4 + e;
+        sh.u[id] = orderable_bits(raw[4 * g + e]);
+        sh.id[id] = (uint32_t)id;
+      }
+    cnt = n < kCap ? n : kCap;
+    first = kCap;
+    wave_sync();
+  }
+  // Two register buffers take turns (the loop is unrolled by two, so no buffer is copied): the
+  // next step's loads are in flight while a step is filtered.  They are unconditional (past n:
+  // loads of the row's start, unused): behind a branch, the wait for a step's keys at the join
+  // would also wait for the next step's loads.
+  uint32_t thr = thr0;
+  uint32_t ring[2][KPL];
+  load_step<KPL, kVec>(row, n, first, ring[0]);
+  bool done = false;
+  for (int s0 = first; !done; s0 += 2 * kStep) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int s = s0 + d * kStep;
+      load_step<KPL, kVec>(row, n, s + kStep, ring[d ^ 1]);
+      uint32_t (&cur)[KPL] = ring[d];
+      const bool more = s < n;
+      int total = 0;
+      if (more) {
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) cur[k] = orderable_bits(cur[k]);
+        if (s + kStep > n) {
+          asm volatile("");  // a branch: only the last step masks its keys past n
+#pragma unroll
+          for (int k = 0; k < KPL; ++k)
+            if (s + ((k >> 2) * 64 + lane) * 4 + (k & 3) >= n) cur[k] = 0u;  // never > thr
+        }
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
+      }
+      if (more ? cnt + total > kCap : cnt > kTopK)
+        thr = wave_keep_top<kCap>(sh, cnt, kTopK, more ? kSlack : 0);
+      if (!more) {
+        done = true;
+        break;
+      }
+      // thr through an empty asm: the comparisons are made again rather than the counting
+      // loop's masks held across the cut
+      uint32_t th = thr;
+      asm volatile("" : "+v"(th));
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) {
+        const bool p = cur[k] > th;
+        const uint64_t m = __ballot(p);
+        // cnt + (keys of this step) <= kCap: the count above, or a cut to <= kCap - kStep
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+        if (p) {
+          sh.u[pos] = cur[k];
+          sh.id[pos] = (uint32_t)(s + ((k >> 2) * 64 + lane) * 4 + (k & 3));
+        }
+        cnt += __popcll(m);
+      }
+    }
+  }
+  wave_sync();
+  return cnt;
+}
+
+// A key value below the row's kSel-th largest, as a rule, from a sample of 2048 of its keys (8
+// runs of 256, one at each eighth of the row): the bin base, in a radix select over the sample,
+// of its k-th largest key, k about 1.5 times the sample's expected share of the kSel largest
+// plus 8; 0 when no estimate is made.  Only a speed-up: the walk counts the keys above it, and
+// when fewer than kSel are, walks the row again without it.  n >= 2048.
+template <int kCap, bool kVec>
+__device__ __forceinline__ uint32_t sample_threshold(const float* row, int n, int kSel,
+                                                     WaveShared<kCap>& sh) {
+  constexpr int SG = 8;  // runs, one 16-byte group of 4 keys per lane each
+  const int lane = threadIdx.x & 63;
+  uint32_t u[4 * SG];
+#pragma unroll
+  for (int j = 0; j < SG; ++j) {
+    const int base = ((int)((int64_t)j * n / SG) & ~3) + 4 * lane;  // base + 3 < n
+    if constexpr (kVec) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + base);
+      u[4 * j + 0] = v.x;
+      u[4 * j + 1] = v.y;
+      u[4 * j + 2] = v.z;
+      u[4 * j + 3] = v.w;
+    } else {
+      const unsigned* r32 = reinterpret_cast<const unsigned*>(row);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * j + e] = r32[base + e];
+    }
+  }
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < 4 * SG; ++i) {
+    u[i] = orderable_bits(u[i]);
+    mn = u[i] < mn ? u[i] : mn;
+    mx = u[i] > mx ? u[i] : mx;
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int kS = (int)((int64_t)kSel * (3 * 64 * 4 * SG) / (2 * (int64_t)n)) + 8;
+  int kRem = kS, inBin = 0;
+  uint32_t lo = mn;
+  wave_window_select<4 * SG>(
+      [&](int i, int c, bool& valid) {
+        valid = true;
+        return u[i];
+      },
+      64 * 4 * SG, sh.hist, lo, mx - mn, kRem, inBin, kS);
+  return lo > 0u ? lo - 1u : 0u;  // keys above it: every key of the chosen bin and above
+}
+
+template <int kCap, int KPL, bool kVec>
+__global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkArgs a) {
   __shared__ WaveShared<kCap> shAll[kWaveRows];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1349,79 +1483,9 @@ __global__ __launch_bounds__(64 * kWaveRows) void topk_expand_wave_kernel(TopkAr
   const float* row = a.logits + i * a.numBlocks;
   int cnt = 0;
   if (n > 0) {
-    // the first min(n, kCap) keys, each at its id
-    {
-      constexpr int FL = kCap / 64;
-      uint32_t raw[FL];
-      load_step<FL, kVec>(row, n, 0, raw);
-#pragma unroll
-      for (int g = 0; g < FL / 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int id = (g * 64 + lane) * 4 + e;
-          sh.u[id] = orderable_bits(raw[4 * g + e]);
-          sh.id[id] = (uint32_t)id;
-        }
-      cnt = n < kCap ? n : kCap;
-    }
-    wave_sync();
-    // The walk.  thr = 0 before the first cut: the buffer then holds kCap >= kTopK real keys
-    // with smaller ids, so a later key with u = 0 is never among the kTopK largest.  The step
-    // past the row's end makes the exact cut to kTopK.
-    // Two register buffers take turns (the loop is unrolled by two, so no buffer is copied):
-    // the next step's loads are in flight while a step is filtered.  They are unconditional
-    // (past n: loads of the row's start, unused): behind a branch, the wait for a step's keys
-    // at the join would also wait for the next step's loads.
-    uint32_t thr = 0u;
-    uint32_t ring[2][KPL];
-    load_step<KPL, kVec>(row, n, kCap, ring[0]);
-    bool done = false;
-    for (int s0 = kCap; !done; s0 += 2 * kStep) {
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int s = s0 + d * kStep;
-        load_step<KPL, kVec>(row, n, s + kStep, ring[d ^ 1]);
-        uint32_t (&cur)[KPL] = ring[d];
-        const bool more = s < n;
-        int total = 0;
-        if (more) {
-#pragma unroll
-          for (int k = 0; k < KPL; ++k) cur[k] = orderable_bits(cur[k]);
-          if (s + kStep > n) {
-            asm volatile("");  // a branch: only the last step masks its keys past n
-#pragma unroll
-            for (int k = 0; k < KPL; ++k)
-              if (s + ((k >> 2) * 64 + lane) * 4 + (k & 3) >= n) cur[k] = 0u;  // never > thr
-          }
-#pragma unroll
-          for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
-        }
-        if (more ? cnt + total > kCap : cnt > kTopK)
-          thr = wave_keep_top<kCap>(sh, cnt, kTopK, more ? kSlack : 0);
-        if (!more) {
-          done = true;
-          break;
-        }
-        // thr through an empty asm: the comparisons are made again rather than the counting
-        // loop's masks held across the cut
-        uint32_t th = thr;
-        asm volatile("" : "+v"(th));
-#pragma unroll
-        for (int k = 0; k < KPL; ++k) {
-          const bool p = cur[k] > th;
-          const uint64_t m = __ballot(p);
-          // cnt + (keys of this step) <= kCap: the count above, or a cut to <= kCap - kStep
-          const int pos = (int)__builtin_amdgcn_mbcnt_hi(
-              (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
-          if (p) {
-            sh.u[pos] = cur[k];
-            sh.id[pos] = (uint32_t)(s + ((k >> 2) * 64 + lane) * 4 + (k & 3));
-          }
-          cnt += __popcll(m);
-        }
-      }
-    }
-    wave_sync();
+    const uint32_t est = n >= 4 * kCap ? sample_threshold<kCap, kVec>(row, n, kSel, sh) : 0u;
+    cnt = walk_row<kCap, KPL, kVec>(row, n, est, sh);
+    if (cnt < kSel) cnt = walk_row<kCap, KPL, kVec>(row, n, 0u, sh);  // estimate too high
   }
   // order the cnt = kSel selected keys: bucket ranks over [T, hi] (their smallest and largest
   // keys), or the bitonic sort when a bucket is crowded; padding composites are 0
