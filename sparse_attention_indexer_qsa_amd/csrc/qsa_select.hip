@@ -285,6 +285,7 @@ __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, 
 
 // The register keys >= T, with their ids, into candU/candId[0, sh.ncand) in an unspecified
 // order (every later use of the candidates is independent of it); sh.ncand must be 0 before.
+// More than kCandCap such keys are counted in sh.ncand but not all stored.
 // Each wave takes its keys in batches of 8 register slots: one comparison per key gives the
 // lane mask that both counts the batch and masks the key's store, and one LDS atomic per batch
 // (by lane 0, on the scalar total) reserves the batch's slots.  Ends with a barrier.
@@ -316,6 +317,7 @@ __device__ __forceinline__ void compact_keys(const uint32_t (&u)[KPT], uint32_t 
       int base = 0;
       if (lane0) base = atomicAdd(&sh.ncand + zero, sum);
       base = __builtin_amdgcn_readfirstlane(base);
+      if (base + sum > kCandCap) continue;  // over capacity (an estimated T): counted only
 #pragma unroll
       for (int b = 0; b < kB; ++b) {
         const int r = k0 + b;
@@ -715,7 +717,8 @@ __device__ __forceinline__ void sort_selected(int m, int kSel, RegShared& sh) {
   __syncthreads();
 }
 
-// Ordering of the m selected composites (keys in [T, hi]) by bucket ranks, where the buckets
+// Ordering of the m selected composites (keys >= T; hi their largest key, or an estimate of it:
+// keys above it share the top bucket) by bucket ranks, where the buckets
 // are small: the key range [T, hi] is cut into kRankBins buckets by its top bits (a bucket's
 // composites all exceed those of every lower bucket), the buckets are counted and laid out in
 // descending order by one block scan, each composite is placed in its bucket, and its rank
@@ -752,8 +755,10 @@ __device__ __forceinline__ void rank_sort(int m, int kSel, uint32_t T, uint32_t 
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     ok[k] = load(k, v[k]);
-    bin[k] = (kRankBins - 1) - (int)(((uint32_t)(v[k] >> 32) - T) >> shift);
-    slot[k] = ok[k] ? (int)atomicAdd(&bins[bin[k] & (kRankBins - 1)], 1u) : 0;
+    // keys above hi (an estimated hi) join the top bucket, which keeps the buckets in order
+    const uint32_t dq = ((uint32_t)(v[k] >> 32) - T) >> shift;
+    bin[k] = dq < (uint32_t)kRankBins ? (kRankBins - 1) - (int)dq : 0;
+    slot[k] = ok[k] ? (int)atomicAdd(&bins[bin[k]], 1u) : 0;
   }
   __syncthreads();
   {
@@ -800,6 +805,73 @@ __device__ __forceinline__ void rank_sort(int m, int kSel, uint32_t T, uint32_t 
   __syncthreads();
 }
 
+// The candidates of a prefill row held in registers from an estimated threshold instead of a
+// radix pass over all its keys: a sample of the first key of every other register group (256 x
+// ceil(KPT / 8) keys spread over the row) gives, by one radix pass over the sample within the
+// window [smallest thread maximum, largest key], the bin of its k-th largest key, k about 1.25
+// times its expected share of the kSel largest plus 10; every key of the row at or above that
+// bin's base T is compacted.  When they number kSel to 2 kTopK, they are the candidates of
+// select_threshold's kCands form (need = -1, hi the sample's largest key: keys above it join
+// the top rank bucket); otherwise need = -2 and the caller runs the exact select.  Three
+// barriers, like the first pass of the exact select; n >= 8 NT (every thread's first two
+// groups are real keys, so each thread's sample maximum is a distinct real key).  Rows short
+// for the kernel (k above NT / 2) return need = -2 at once.
+template <int NT, int KPT>
+__device__ __forceinline__ Threshold estimate_candidates(const uint32_t (&u)[KPT], int n, int kSel,
+                                                        RegShared& sh) {
+  constexpr int NS = (KPT / 4 + 1) / 2;  // sample keys per thread: groups 0, 2, 4, ...
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // at least NT sample keys are >= lo (the threads' maxima, below); too large a k for that
+  // (rows short for the kernel's registers) takes the exact select
+  const int kS = (int)((int64_t)kSel * (5 * NT * NS) / (4 * (int64_t)n)) + 10;
+  if (kS > NT / 2) return Threshold{0u, -2, 0, -1, 0u};
+  uint32_t tmax = 0u;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) tmax = u[8 * j] > tmax ? u[8 * j] : tmax;
+  uint32_t wmax = tmax, wmin = tmax;
+  auto step = [&](int o) {
+    const uint32_t a = xor_lane(wmax, o), b = xor_lane(wmin, o);
+    wmax = a > wmax ? a : wmax;
+    wmin = b < wmin ? b : wmin;
+  };
+  step(32);
+  step(16);
+  step(8);
+  step(4);
+  step(2);
+  step(1);
+  if (lane == 0) {
+    sh.red[0][wave] = wmax;
+    sh.red[1][wave] = wmin;
+  }
+  for (int j = tid; j < 256; j += NT) sh.hist[0][j] = 0;
+  if (tid == 0) sh.ncand = 0;
+  __syncthreads();
+  uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    hi = sh.red[0][w] > hi ? sh.red[0][w] : hi;
+    lo = sh.red[1][w] < lo ? sh.red[1][w] : lo;
+  }
+  const uint32_t wm1 = hi - lo;
+  const int bits = wm1 ? 32 - __clz(wm1) : 0;
+  const int shift = bits > 8 ? bits - 8 : 0;
+  int one = 1;
+  asm volatile("" : "+v"(one));
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const uint32_t d = u[8 * j] - lo;
+    if (d <= wm1) atomicAdd(&sh.hist[0][d >> shift], one);
+  }
+  __syncthreads();
+  const BinPick pick = find_bin(sh.hist[0], kS);
+  const uint32_t T = lo + ((uint32_t)pick.bin << shift);
+  compact_keys<NT, KPT>(u, T, sh);
+  const int nc = sh.ncand;
+  if (nc >= kSel && nc <= 2 * kTopK) return Threshold{T, -1, 0, nc, hi};
+  return Threshold{T, -2, 0, -1, hi};
+}
+
 // Waves per SIMD the register allocation aims for at KPT keys per thread (512 VGPRs per SIMD
 // lane shared by the waves): at most 80 keys leave room for 4 rows of 4 waves on a CU.
 constexpr int reg_waves(int kpt) { return kpt <= 24 ? 5 : kpt <= 80 ? 4 : kpt <= 96 ? 3 : 2; }
@@ -833,7 +905,10 @@ void topk_expand_reg_kernel(TopkArgs a) {
     sort_selected<kTopK / kRT>(n, kSel, sh);
   } else {
     clear_rank_bins(sh);  // ordered before rank_sort by the select's barriers
-    const Threshold th = select_threshold<kRT, KPT, true>(u, n, kSel, sh);
+    Threshold th{0u, -2, 0, -1, 0u};
+    if constexpr (KPT >= 16)
+      if (n >= 8 * kRT) th = estimate_candidates<kRT, KPT>(u, n, kSel, sh);
+    if (th.need == -2) th = select_threshold<kRT, KPT, true>(u, n, kSel, sh);
     const uint32_t T = th.T;
     const int m = (kSel - th.need) + th.ties;
     if (th.need < 0) {
