@@ -184,10 +184,12 @@ def test_topk_expand_rank_paths(qsa, O):
     (too many candidates: the exact threshold, the ordered pass over the row, one large bucket);
     900 tied under 100 distinct (1000 candidates, one large bucket); and 1100 distinct keys
     one ulp apart (more than 1024 candidates: the exact threshold from the LDS passes, then the
-    ranks of the keys at or above it)."""
+    ranks of the keys at or above it); and a row whose only large keys sit where the register
+    kernel samples (the first key of every other register group), so that the sample's estimate
+    leaves fewer than 512 keys above it and the exact select runs instead."""
     B, S, nb = 1, 70000, 17500
     ctx = np.array([S], np.int32)
-    r0, n = S - 5, 5
+    r0, n = S - 6, 6
     rng = np.random.default_rng(31)
     logits = rng.standard_normal((n, nb)).astype(np.float32)
     five = np.array([5.0], np.float32).view(np.uint32)[0]
@@ -201,7 +203,34 @@ def test_topk_expand_rank_paths(qsa, O):
         logits[row, pos[:tied]] = np.float32(5.0)
         if distinct:
             logits[row, pos[tied:]] = above(distinct, 1 if tied else 0)
+    ids = np.arange(nb)
+    sampled = (ids % 4 == 0) & ((ids // 1024) % 2 == 0)  # 256 threads x 4 keys per group
+    logits[5, sampled] += np.float32(10.0)
     _run_long(qsa, O, B, S, nb, ctx, r0, n, logits, "rank paths")
+
+
+def test_topk_expand_wave_estimate_fallback(qsa, O):
+    """Rows past the register kernel (one wave per row) whose only large keys sit in the runs
+    the walk samples for its start threshold (256 keys at each eighth of the row): the estimate
+    then leaves fewer than 512 keys above it and the row is walked again from the plain start.
+    Beside each, a row of the same length with the large keys elsewhere; 16-byte aligned rows
+    and rows of one load per key."""
+    for S, nb in ((80000, 20000), (80004, 20001)):
+        ctx = np.array([S], np.int32)
+        r0, n = S - 4, 4
+        rng = np.random.default_rng(37)
+        logits = rng.standard_normal((n, nb)).astype(np.float32)
+        for row in range(n):
+            nv = min((r0 + row + 1) // 4, nb)
+            runs = np.zeros(nb, bool)
+            for j in range(8):
+                p = (j * nv // 8) & ~3
+                runs[p:p + 256] = True
+            if row % 2 == 0:
+                logits[row, runs] += np.float32(10.0)
+            else:
+                logits[row, np.flatnonzero(~runs[:nv])[:2048]] += np.float32(10.0)
+        _run_long(qsa, O, 1, S, nb, ctx, r0, n, logits, f"wave estimate fallback nb={nb}")
 
 
 def test_topk_expand_all_ones_nan(qsa, O):
