@@ -1448,6 +1448,9 @@ __device__ __forceinline__ int walk_row(const float* row, int n, uint32_t thr0,
       load_step<KPL, kVec>(row, n, s + kStep, ring[d ^ 1]);
       uint32_t (&cur)[KPL] = ring[d];
       const bool more = s < n;
+      // the step is counted first only when it might not fit: a buffer with room for a whole
+      // step takes it as it is
+      const bool mightOverflow = cnt + kStep > kCap;
       int total = 0;
       if (more) {
 #pragma unroll
@@ -1458,8 +1461,10 @@ __device__ __forceinline__ int walk_row(const float* row, int n, uint32_t thr0,
           for (int k = 0; k < KPL; ++k)
             if (s + ((k >> 2) * 64 + lane) * 4 + (k & 3) >= n) cur[k] = 0u;  // never > thr
         }
+        if (mightOverflow) {
 #pragma unroll
-        for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
+          for (int k = 0; k < KPL; ++k) total += __popcll(__ballot(cur[k] > thr));
+        }
       }
       if (more ? cnt + total > kCap : cnt > kTopK)
         thr = wave_keep_top<kCap>(sh, cnt, kTopK, more ? kSlack : 0);
@@ -1475,7 +1480,8 @@ __device__ __forceinline__ int walk_row(const float* row, int n, uint32_t thr0,
       for (int k = 0; k < KPL; ++k) {
         const bool p = cur[k] > th;
         const uint64_t m = __ballot(p);
-        // cnt + (keys of this step) <= kCap: the count above, or a cut to <= kCap - kStep
+        // cnt + (keys of this step) <= kCap: room for a whole step, the count above, or a cut
+        // to <= kCap - kStep
         const int pos = (int)__builtin_amdgcn_mbcnt_hi(
             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
         if (p) {
