@@ -209,6 +209,20 @@ def test_topk_expand_rank_paths(qsa, O):
     _run_long(qsa, O, B, S, nb, ctx, r0, n, logits, "rank paths")
 
 
+def test_topk_expand_estimate_boundary(qsa, O):
+    """One launch of the 48-keys-per-thread register kernel over rows of 8200 to 8500 blocks in
+    four value styles: rows below about 8330 blocks take the exact select (the sample's k would
+    exceed half the threads), longer ones the sampled first pass; bit-exact against the oracle
+    either way, on 16-byte aligned rows and on rows of one load per key."""
+    for nb in (8528, 8525):
+        S = 34100
+        ctx = np.array([S], np.int32)
+        r0, n = 32800, 1200
+        logits = W.prefill_logits(19, ctx, S, nb, r0, n,
+                                  ("scores", "normal", "ties", "special_ge"))
+        _run_long(qsa, O, 1, S, nb, ctx, r0, n, logits, f"estimate boundary nb={nb}")
+
+
 def test_topk_expand_wave_estimate_fallback(qsa, O):
     """Rows past the register kernel (one wave per row) whose only large keys sit in the runs
     the walk samples for its start threshold (256 keys at each eighth of the row): the estimate
