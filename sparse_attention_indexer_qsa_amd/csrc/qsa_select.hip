@@ -1101,6 +1101,7 @@ constexpr int kWaveRows = 4;       // rows (waves) per workgroup of the one-wave
 // per CU (36 KB of LDS per workgroup); longer ones a larger buffer and steps, so fewer cuts
 constexpr int kWaveCapMid = 1024, kWaveKPLMid = 4;    // 256 keys per step
 constexpr int kWaveCapLong = 1536, kWaveKPLLong = 8;  // 512 keys per step
+constexpr int kWaveDepth = 2;  // steps of keys in registers: one filtered, the rest loading
 
 template <int kCap>
 struct WaveShared {
@@ -1376,25 +1377,32 @@ __device__ __forceinline__ bool rank_wave(const uint64_t (&v)[E], int m, uint32_
 }
 
 // KPL keys per lane of the step starting at id s: lane l takes the 16-byte groups
-// s + 4 (g * 64 + l).  kVec: one 16-byte load per group (groups past n load the row's first
-// keys); otherwise one load per key at min(id, n - 1).  Raw FP32 bits; the caller masks.
+// s + 4 (g * 64 + l).  kVec: one 16-byte load per group; otherwise one load per key.  The loads
+// go through a buffer resource that starts at key s and ends at key n (kVec: rounded up to a
+// whole 16-byte group, which the row holds), so that keys past it read as 0 without touching
+// memory; its base and size are scalar, and the lane's offset is the same in every step.  Raw
+// FP32 bits, non-temporal; the caller masks.
 template <int KPL, bool kVec>
 __device__ __forceinline__ void load_step(const float* row, int n, int s, uint32_t (&raw)[KPL]) {
   const int lane = threadIdx.x & 63;
+  const int left = 4 * ((kVec ? (n + 3) & ~3 : n) - s);  // bytes from key s to the end
+  // data format 32 bits (the field must be non-zero for untyped accesses)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(row) + s, 0, left > 0 ? left : 0, 0x00020000);
 #pragma unroll
   for (int g = 0; g < KPL / 4; ++g) {
-    const int base = s + (g * 64 + lane) * 4;
     if constexpr (kVec) {
-      const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(row + (base < n ? base : 0)));
+      const u32x4 v = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane + 1024 * g, 0, 2));
       raw[4 * g + 0] = v.x;
       raw[4 * g + 1] = v.y;
       raw[4 * g + 2] = v.z;
       raw[4 * g + 3] = v.w;
     } else {
-      const unsigned* r32 = reinterpret_cast<const unsigned*>(row);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) raw[4 * g + e] = __builtin_nontemporal_load(r32 + min(base + e, n - 1));
+      for (int e = 0; e < 4; ++e)
+        raw[4 * g + e] =
+            __builtin_amdgcn_raw_buffer_load_b32(rs, 16 * lane + 1024 * g + 4 * e, 0, 2);
     }
   }
 }
@@ -1433,19 +1441,21 @@ __device__ __forceinline__ int walk_row(const float* row, int n, uint32_t thr0,
     first = kCap;
     wave_sync();
   }
-  // Two register buffers take turns (the loop is unrolled by two, so no buffer is copied): the
-  // next step's loads are in flight while a step is filtered.  They are unconditional (past n:
-  // loads of the row's start, unused): behind a branch, the wait for a step's keys at the join
-  // would also wait for the next step's loads.
+  // kWaveDepth register buffers take turns (the loop is unrolled by that many, so no buffer is
+  // copied): the loads of the next kWaveDepth - 1 steps are in flight while a step is
+  // filtered.  They are unconditional (past n they read nothing and give 0): behind a branch,
+  // the wait for a step's keys at the join would also wait for the later steps' loads.
+  constexpr int D = kWaveDepth;
   uint32_t thr = thr0;
-  uint32_t ring[2][KPL];
-  load_step<KPL, kVec>(row, n, first, ring[0]);
-  bool done = false;
-  for (int s0 = first; !done; s0 += 2 * kStep) {
+  uint32_t ring[D][KPL];
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
+  for (int d = 0; d + 1 < D; ++d) load_step<KPL, kVec>(row, n, first + d * kStep, ring[d]);
+  bool done = false;
+  for (int s0 = first; !done; s0 += D * kStep) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
       const int s = s0 + d * kStep;
-      load_step<KPL, kVec>(row, n, s + kStep, ring[d ^ 1]);
+      load_step<KPL, kVec>(row, n, s + (D - 1) * kStep, ring[(d + D - 1) % D]);
       uint32_t (&cur)[KPL] = ring[d];
       const bool more = s < n;
       // the step is counted first only when it might not fit: a buffer with room for a whole
