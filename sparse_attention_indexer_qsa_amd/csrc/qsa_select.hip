@@ -181,39 +181,49 @@ __device__ __forceinline__ int wave_suffix(int x) {
 
 // The row's keys into registers (padding u = 0).  No load sits behind a branch, so the
 // compiler keeps several in flight (a per-group branch had it wait for each load in turn).
-// kVec: rows 16-byte aligned with a length that is a multiple of 4, so a group that starts
-// before n ends inside the row and is one 16-byte load (groups wholly past n load the row's
-// first keys).  Otherwise one load per key at min(id, n - 1).  Keys past n are masked to 0.
+// Group g of thread tid holds keys 4 (g NT + tid) + e, e < 4.  Each group's loads go through a
+// buffer resource that starts at the group's first key and ends at key n, so keys past n read
+// as 0 without touching memory: no address clamp, and a thread's offset is the same in every
+// group.  kVec: rows 16-byte aligned with a length that is a multiple of 4, the resource's end
+// rounded up to a whole 16-byte group (inside the row), one 16-byte load per group; otherwise
+// one load per key.  Keys past n are masked to 0, only in the groups that reach past n.
 template <int NT, int KPT, bool kVec>
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&u)[KPT]) {
   const int tid = threadIdx.x;
+  const int nr = kVec ? (n + 3) & ~3 : n;  // keys the resources cover
   // every load first, into the key registers themselves, so that all of them are in flight
   // together; the scheduling fence keeps the compiler from mapping (and so waiting for) the
   // first groups while later loads are still to be issued
 #pragma unroll
   for (int g = 0; g < KPT / 4; ++g) {
-    const int base = (g * NT + tid) * 4;
-    const int lim = n - base;  // keys of this group inside the row (<= 0: none)
+    const int left = 4 * (nr - g * NT * 4);  // bytes from the group's first key to the end
+    // data format 32 bits (the field must be non-zero for untyped accesses)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row) + g * NT * 4, 0, left > 0 ? left : 0, 0x00020000);
     if constexpr (kVec) {
-      const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(row + (lim > 0 ? base : 0)));
+      const u32x4 v = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, 0, 2));  // non-temporal
       u[4 * g + 0] = v.x;
       u[4 * g + 1] = v.y;
       u[4 * g + 2] = v.z;
       u[4 * g + 3] = v.w;
     } else {
-      const unsigned* r32 = reinterpret_cast<const unsigned*>(row);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        u[4 * g + e] = __builtin_nontemporal_load(r32 + min(base + e, n - 1));
+        u[4 * g + e] = __builtin_amdgcn_raw_buffer_load_b32(rs, 16 * tid + 4 * e, 0, 2);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int g = 0; g < KPT / 4; ++g) {
-    const int lim = n - (g * NT + tid) * 4;
+    if (n >= (g + 1) * NT * 4) {  // uniform: every thread's group lies inside the row
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[4 * g + e] = lim > e ? orderable_bits(u[4 * g + e]) : 0u;
+      for (int e = 0; e < 4; ++e) u[4 * g + e] = orderable_bits(u[4 * g + e]);
+    } else {
+      const int lim = n - (g * NT + tid) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * g + e] = lim > e ? orderable_bits(u[4 * g + e]) : 0u;
+    }
   }
 }
 
