@@ -296,15 +296,13 @@ __device__ __forceinline__ int compact(Pred pred, Store store, Refresh refresh, 
 // The register keys >= T, with their ids, into candU/candId[0, sh.ncand) in an unspecified
 // order (every later use of the candidates is independent of it); sh.ncand must be 0 before.
 // More than kCandCap such keys are counted in sh.ncand but not all stored.
-// Each wave takes its keys in batches of 8 register slots: one comparison per key gives the
-// lane mask that both counts the batch and masks the key's store, and one LDS atomic per batch
-// (by lane 0, on the scalar total) reserves the batch's slots.  Ends with a barrier.
+// Each thread counts its keys >= T, a wave prefix of the counts gives every thread its first
+// slot in the wave's run, one LDS atomic (by lane 0, on the wave's total) reserves the run, and
+// each thread then stores its keys one after another: per key one comparison, and a store only
+// where some lane of the wave stores.  Ends with a barrier.
 template <int NT, int KPT>
 __device__ __forceinline__ void compact_keys(const uint32_t (&u)[KPT], uint32_t T,
                                              RegShared& sh) {
-  constexpr int kBatch = 8;
-  static_assert(KPT % kBatch == 0 || KPT < kBatch, "whole batches of register keys");
-  constexpr int kB = KPT < kBatch ? KPT : kBatch;
   // 4 * tid through an empty asm: each key's id is then one add of a constant
   int ft4 = fresh_tid() << 2;
   asm volatile("" : "+v"(ft4));
@@ -312,29 +310,23 @@ __device__ __forceinline__ void compact_keys(const uint32_t (&u)[KPT], uint32_t 
   // one-lane atomic is not rewritten into a wave reduction
   int zero = 0;
   asm volatile("" : "+v"(zero));
-  const bool lane0 = (threadIdx.x & 63) == 0;
+  int c = 0;
 #pragma unroll
-  for (int k0 = 0; k0 < KPT; k0 += kB) {
-    uint64_t m[kB];
-    int pre[kB], sum = 0;
+  for (int r = 0; r < KPT; ++r) c += u[r] >= T ? 1 : 0;
+  const int incl = wave_prefix(c);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  if (total != 0) {  // wave-uniform
+    int base = 0;
+    if ((threadIdx.x & 63) == 0) base = atomicAdd(&sh.ncand + zero, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (base + total <= kCandCap) {  // else over capacity (an estimated T): counted only
+      int pos = base + incl - c;
 #pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      m[b] = __ballot(u[k0 + b] >= T);
-      pre[b] = sum;
-      sum += __popcll(m[b]);
-    }
-    if (sum != 0) {  // wave-uniform
-      int base = 0;
-      if (lane0) base = atomicAdd(&sh.ncand + zero, sum);
-      base = __builtin_amdgcn_readfirstlane(base);
-      if (base + sum > kCandCap) continue;  // over capacity (an estimated T): counted only
-#pragma unroll
-      for (int b = 0; b < kB; ++b) {
-        const int r = k0 + b;
-        if (u[r] >= T) {  // the comparison of the ballot above
-          const int pos = base + pre[b] + lanes_below(m[b]);
+      for (int r = 0; r < KPT; ++r) {
+        if (u[r] >= T) {
           sh.candU[pos] = u[r];
           sh.candId[pos] = ft4 + ((r >> 2) * NT * 4 + (r & 3));  // key_id<NT>(r, tid)
+          ++pos;
         }
       }
     }
