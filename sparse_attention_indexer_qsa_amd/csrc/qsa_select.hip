@@ -1508,15 +1508,15 @@ __device__ __forceinline__ int walk_row(const float* row, int n, uint32_t thr0,
   return cnt;
 }
 
-// A key value below the row's kSel-th largest, as a rule, from a sample of 2048 of its keys (8
-// runs of 256, one at each eighth of the row): the bin base, in a radix select over the sample,
+// A key value below the row's kSel-th largest, as a rule, from a sample of 1024 of its keys (4
+// runs of 256, one at each quarter of the row): the bin base, in a radix select over the sample,
 // of its k-th largest key, k about 1.5 times the sample's expected share of the kSel largest
 // plus 8; 0 when no estimate is made.  Only a speed-up: the walk counts the keys above it, and
-// when fewer than kSel are, walks the row again without it.  n >= 2048.
+// when fewer than kSel are, walks the row again without it.  n >= 1024.
 template <int kCap, bool kVec>
 __device__ __forceinline__ uint32_t sample_threshold(const float* row, int n, int kSel,
                                                      WaveShared<kCap>& sh) {
-  constexpr int SG = 8;  // runs, one 16-byte group of 4 keys per lane each
+  constexpr int SG = 4;  // runs, one 16-byte group of 4 keys per lane each
   const int lane = threadIdx.x & 63;
   uint32_t u[4 * SG];
 #pragma unroll

@@ -224,9 +224,10 @@ def test_topk_expand_estimate_boundary(qsa, O):
 
 
 def test_topk_expand_wave_estimate_fallback(qsa, O):
-    """Rows past the register kernel (one wave per row) whose only large keys sit in the runs
-    the walk samples for its start threshold (256 keys at each eighth of the row): the estimate
-    then leaves fewer than 512 keys above it and the row is walked again from the plain start.
+    """Rows past the register kernel (one wave per row) whose only large keys sit in runs of
+    256 at each eighth of the row, which include the runs the walk samples for its start
+    threshold (one at each quarter): the estimate then leaves fewer than 512 keys above it and
+    the row is walked again from the plain start.
     Beside each, a row of the same length with the large keys elsewhere; 16-byte aligned rows
     and rows of one load per key."""
     for S, nb in ((80000, 20000), (80004, 20001)):
